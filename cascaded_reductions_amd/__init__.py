@@ -1,0 +1,241 @@
+"""Python binding of librf (fused cascaded reductions on MI355X).
+
+A thin ctypes layer over the C ABI in include/librf.h: it checks tensor dtype,
+device, shape and contiguity, passes data pointers and the current HIP stream,
+and turns a non-zero status into RFError. All arithmetic happens in the HIP
+kernels; torch provides device memory and streams only. There is no fallback:
+if librf.so is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "RFError", "load", "lib_path", "RF_F32", "RF_BF16",
+    "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode",
+    "moe_route", "quant_gemm", "quant_gemm_workspace_size",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RF_F32, RF_BF16 = 0, 1
+_STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARGUMENT", 2: "RF_ERR_UNSUPPORTED",
+           3: "RF_ERR_BUFFER_TOO_SMALL", 4: "RF_ERR_DEVICE"}
+
+
+class RFError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+
+
+def lib_path() -> str:
+    return os.path.join(HERE, "librf.so")
+
+
+_lib = None
+_c = ctypes
+_P, _I64, _F, _SZ = _c.c_void_p, _c.c_int64, _c.c_float, _c.c_size_t
+_SIGS = {
+    "rf_abi_version": ([], _c.c_int),
+    "rf_status_string": ([_c.c_int], _c.c_char_p),
+    "rf_last_error": ([], _c.c_char_p),
+    "rf_softmax_gemm_fused": ([_c.c_int, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P], _c.c_int),
+    "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
+    "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
+    "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
+    "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "rf_quant_gemm": ([_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
+}
+
+
+def load():
+    """Load librf.so (once) and declare every exported signature. Raises RFError if absent."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RFError(-1, f"{path} is not built (python -m cascaded_reductions_amd.build)")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes, fn.restype = args, res
+        if lib.rf_abi_version() != 1:
+            raise RFError(-1, f"unexpected ABI version {lib.rf_abi_version()}")
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RFError(status, load().rf_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _need(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else _c.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return _c.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+# ------------------------------------------------------------------ attention
+
+
+def softmax_gemm_fused(q, k, v, scale: float | None = None, *, out=None, lse=None, return_lse: bool = True):
+    """O = softmax(scale * Q K^T) V for q [B,H,Sq,D], k/v [B,H,Sk,D] (fp32 or bf16).
+
+    Returns (o, lse) with lse [B,H,Sq] fp32 (None if return_lse is False and no lse is given)."""
+    torch = _torch()
+    dt = q.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Sq, D]")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2] if k.dim() == 4 else -1
+    _need(q, "q", dt)
+    _need(k, "k", dt, (B, H, Sk, D))
+    _need(v, "v", dt, (B, H, Sk, D))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dt, q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H, Sq))
+    _check(load().rf_softmax_gemm_fused(RF_F32 if dt == torch.float32 else RF_BF16, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(out), _ptr(lse), B, H, Sq, Sk, D, float(scale), _stream(q)))
+    return out, lse
+
+
+def attn_decode_split(q, k, v, nseg: int, scale: float | None = None, *, part_m=None, part_s=None, part_o=None):
+    """Per-segment partials for q [B,H,D], k/v [B,H,L,D] bf16. Returns (part_m, part_s, part_o)."""
+    torch = _torch()
+    B, H, D = q.shape
+    L = k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, H, L, D))
+    _need(v, "v", torch.bfloat16, (B, H, L, D))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    part_m = torch.empty((B * H, nseg), dtype=torch.float32, device=dev) if part_m is None else part_m
+    part_s = torch.empty((B * H, nseg), dtype=torch.float32, device=dev) if part_s is None else part_s
+    part_o = torch.empty((B * H, nseg, D), dtype=torch.float32, device=dev) if part_o is None else part_o
+    _need(part_m, "part_m", torch.float32, (B * H, nseg))
+    _need(part_s, "part_s", torch.float32, (B * H, nseg))
+    _need(part_o, "part_o", torch.float32, (B * H, nseg, D))
+    _check(load().rf_attn_decode_split(_ptr(q), _ptr(k), _ptr(v), B, H, L, D, nseg, float(scale),
+                                       _ptr(part_m), _ptr(part_s), _ptr(part_o), _stream(q)))
+    return part_m, part_s, part_o
+
+
+def segment_merge(part_m, part_s, part_o, out_dtype=None, *, out=None, lse=None, return_lse: bool = True):
+    """Merge partials [R,T], [R,T], [R,T,D] -> (o [R,D] in out_dtype, lse [R])."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    R, T, D = part_o.shape
+    _need(part_m, "part_m", torch.float32, (R, T))
+    _need(part_s, "part_s", torch.float32, (R, T))
+    _need(part_o, "part_o", torch.float32, (R, T, D))
+    out = torch.empty((R, D), dtype=out_dtype, device=part_o.device) if out is None else out
+    _need(out, "out", out_dtype, (R, D))
+    if lse is None and return_lse:
+        lse = torch.empty((R,), dtype=torch.float32, device=part_o.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (R,))
+    _check(load().rf_segment_merge(_ptr(part_m), _ptr(part_s), _ptr(part_o), R, T, D,
+                                   RF_F32 if out_dtype == torch.float32 else RF_BF16, _ptr(out), _ptr(lse),
+                                   _stream(part_o)))
+    return out, lse
+
+
+def attn_decode(q, k, v, nseg: int, scale: float | None = None, out_dtype=None):
+    """Split + merge on the current stream: returns (o [B,H,D], lse [B,H])."""
+    B, H, D = q.shape
+    pm, ps, po = attn_decode_split(q, k, v, nseg, scale)
+    o, lse = segment_merge(pm, ps, po, out_dtype)
+    return o.view(B, H, D), lse.view(B, H)
+
+
+# ------------------------------------------------------------------ MoE gate
+
+
+def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False):
+    """x [T,Hd] bf16, w_gate [Hd,E] bf16 -> (idx [T,k] int32, w [T,k] fp32, scores [T,E] fp32 or None)."""
+    torch = _torch()
+    T, Hd = x.shape
+    E = w_gate.shape[1]
+    _need(x, "x", torch.bfloat16)
+    _need(w_gate, "w_gate", torch.bfloat16, (Hd, E))
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if w is None else w
+    _need(idx, "idx", torch.int32, (T, k))
+    _need(w, "w", torch.float32, (T, k))
+    if scores is None and return_scores:
+        scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, (T, E))
+    _check(load().rf_moe_route(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores), _stream(x)))
+    return idx, w, scores
+
+
+# ------------------------------------------------------------------ dynamic FP8 quant GEMM
+
+
+def quant_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(load().rf_quant_gemm_workspace_size(M, N, K))
+
+
+def quant_gemm(x, wq, w_scale, *, y=None, x_scale=None, xq=None, workspace=None, return_codes: bool = False):
+    """x [M,K] bf16, wq [N,K] uint8 (E4M3FN codes), w_scale [N] fp32 -> (y [M,N] bf16, x_scale [M], xq or None)."""
+    torch = _torch()
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(wq, "wq", torch.uint8, (N, K))
+    _need(w_scale, "w_scale", torch.float32, (N,))
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    _need(y, "y", torch.bfloat16, (M, N))
+    _need(x_scale, "x_scale", torch.float32, (M,))
+    if xq is None and return_codes:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if xq is not None:
+        _need(xq, "xq", torch.uint8, (M, K))
+    ws_bytes = 0
+    if xq is None:
+        need = quant_gemm_workspace_size(M, N, K)
+        if workspace is None and need:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().rf_quant_gemm(_ptr(x), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y), _ptr(x_scale), _ptr(xq),
+                                _ptr(workspace), ws_bytes, _stream(x)))
+    return y, x_scale, xq

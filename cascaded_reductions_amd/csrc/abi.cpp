@@ -1,0 +1,272 @@
+// The C ABI of librf: argument validation (pure host code, no HIP call before
+// it has passed), status text, the thread-local error message, and dispatch to
+// the kernel launchers.
+#include "librf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string t_err;
+
+rf_status fail(rf_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return s;
+}
+
+rf_status ok() {
+    t_err.clear();
+    return RF_OK;
+}
+
+rf_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(RF_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// a*b*... without overflow for the (positive, bounded) sizes accepted here.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool prod(std::initializer_list<int64_t> xs, int64_t* out) {
+    int64_t p = 1;
+    for (int64_t x : xs)
+        if (!mul_ok(p, x, &p)) return false;
+    *out = p;
+    return true;
+}
+
+#define RF_REQUIRE(cond, status, ...)                     \
+    do {                                                  \
+        if (!(cond)) return fail((status), __VA_ARGS__);  \
+    } while (0)
+
+#define RF_PTR(p, name)                                                                        \
+    do {                                                                                       \
+        RF_REQUIRE((p) != nullptr, RF_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);      \
+        RF_REQUIRE(aligned16(p), RF_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name); \
+    } while (0)
+
+#define RF_OPT_PTR(p, name)                                                                    \
+    do {                                                                                       \
+        if (p) RF_REQUIRE(aligned16(p), RF_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name); \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int rf_abi_version(void) { return RF_ABI_VERSION; }
+
+const char* rf_status_string(rf_status s) {
+    switch (s) {
+        case RF_OK: return "RF_OK";
+        case RF_ERR_INVALID_ARGUMENT: return "RF_ERR_INVALID_ARGUMENT";
+        case RF_ERR_UNSUPPORTED: return "RF_ERR_UNSUPPORTED";
+        case RF_ERR_BUFFER_TOO_SMALL: return "RF_ERR_BUFFER_TOO_SMALL";
+        case RF_ERR_DEVICE: return "RF_ERR_DEVICE";
+    }
+    return "RF_STATUS_UNKNOWN";
+}
+
+const char* rf_last_error(void) { return t_err.c_str(); }
+
+rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const void* v,
+                                void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
+                                int64_t Sk, int64_t D, float scale, rf_stream stream) {
+    RF_REQUIRE(dt == RF_F32 || dt == RF_BF16, RF_ERR_INVALID_ARGUMENT, "dt must be RF_F32 or RF_BF16");
+    RF_PTR(q, "q");
+    RF_PTR(k, "k");
+    RF_PTR(v, "v");
+    RF_PTR(o, "o");
+    RF_OPT_PTR(lse, "lse");
+    RF_REQUIRE(B >= 1 && H >= 1 && Sq >= 1 && Sk >= 1, RF_ERR_INVALID_ARGUMENT,
+               "B, H, Sq and Sk must be >= 1 (got %lld, %lld, %lld, %lld)", (long long)B,
+               (long long)H, (long long)Sq, (long long)Sk);
+    RF_REQUIRE(D >= 1, RF_ERR_INVALID_ARGUMENT, "D must be >= 1");
+    RF_REQUIRE(D == 64 || D == 128, RF_ERR_UNSUPPORTED, "D must be 64 or 128 (got %lld)", (long long)D);
+    RF_REQUIRE(scale == scale && scale - scale == 0.0f, RF_ERR_INVALID_ARGUMENT, "scale must be finite");
+    int64_t nq, nk, nl;
+    RF_REQUIRE(prod({B, H, Sq, D}, &nq) && nq < kMaxElems && prod({B, H, Sk, D}, &nk) &&
+                   nk < kMaxElems && prod({B, H, Sq}, &nl),
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    const uint64_t es = dt == RF_F32 ? 4 : 2;
+    RF_REQUIRE(!overlap(o, nq * es, q, nq * es) && !overlap(o, nq * es, k, nk * es) &&
+                   !overlap(o, nq * es, v, nk * es) && !overlap(lse, nl * 4, q, nq * es) &&
+                   !overlap(lse, nl * 4, k, nk * es) && !overlap(lse, nl * 4, v, nk * es) &&
+                   !overlap(lse, nl * 4, o, nq * es),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == RF_F32)
+        e = rf::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<float*>(o), lse,
+                                    B * H, Sq, Sk, int(D), scale, s);
+    else
+        e = rf::launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                     B * H, Sq, Sk, int(D), scale, s);
+    return device_status(e, "rf_softmax_gemm_fused launch");
+}
+
+rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int64_t B,
+                               int64_t H, int64_t L, int64_t D, int64_t nseg, float scale,
+                               float* part_m, float* part_s, float* part_o, rf_stream stream) {
+    RF_PTR(q, "q");
+    RF_PTR(k, "k");
+    RF_PTR(v, "v");
+    RF_PTR(part_m, "part_m");
+    RF_PTR(part_s, "part_s");
+    RF_PTR(part_o, "part_o");
+    RF_REQUIRE(B >= 1 && H >= 1 && L >= 1, RF_ERR_INVALID_ARGUMENT,
+               "B, H and L must be >= 1 (got %lld, %lld, %lld)", (long long)B, (long long)H, (long long)L);
+    RF_REQUIRE(nseg >= 1 && nseg <= L, RF_ERR_INVALID_ARGUMENT, "need 1 <= nseg <= L (nseg=%lld, L=%lld)",
+               (long long)nseg, (long long)L);
+    RF_REQUIRE(D >= 1, RF_ERR_INVALID_ARGUMENT, "D must be >= 1");
+    RF_REQUIRE(D == 64 || D == 128, RF_ERR_UNSUPPORTED, "D must be 64 or 128 (got %lld)", (long long)D);
+    RF_REQUIRE(scale == scale && scale - scale == 0.0f, RF_ERR_INVALID_ARGUMENT, "scale must be finite");
+    int64_t rows, kv, np, npo;
+    RF_REQUIRE(prod({B, H}, &rows) && prod({rows, L, D}, &kv) && kv < (int64_t(1) << 46) &&
+                   prod({rows, nseg}, &np) && np <= INT32_MAX && prod({np, D}, &npo),
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    RF_REQUIRE(!overlap(part_m, np * 4, part_s, np * 4) && !overlap(part_m, np * 4, part_o, npo * 4) &&
+                   !overlap(part_s, np * 4, part_o, npo * 4) && !overlap(part_o, npo * 4, k, kv * 2) &&
+                   !overlap(part_o, npo * 4, v, kv * 2) && !overlap(part_o, npo * 4, q, rows * D * 2) &&
+                   !overlap(part_m, np * 4, k, kv * 2) && !overlap(part_m, np * 4, v, kv * 2) &&
+                   !overlap(part_s, np * 4, k, kv * 2) && !overlap(part_s, np * 4, v, kv * 2) &&
+                   !overlap(part_m, np * 4, q, rows * D * 2) && !overlap(part_s, np * 4, q, rows * D * 2),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipError_t e = rf::launch_decode_split(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), rows, L, int(D), nseg, scale,
+                                           part_m, part_s, part_o, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_attn_decode_split launch");
+}
+
+rf_status rf_segment_merge(const float* part_m, const float* part_s, const float* part_o,
+                           int64_t rows, int64_t nseg, int64_t D, rf_dtype out_dt, void* o,
+                           float* lse, rf_stream stream) {
+    RF_PTR(part_m, "part_m");
+    RF_PTR(part_s, "part_s");
+    RF_PTR(part_o, "part_o");
+    RF_PTR(o, "o");
+    RF_OPT_PTR(lse, "lse");
+    RF_REQUIRE(out_dt == RF_F32 || out_dt == RF_BF16, RF_ERR_INVALID_ARGUMENT, "out_dt must be RF_F32 or RF_BF16");
+    RF_REQUIRE(rows >= 1 && nseg >= 1, RF_ERR_INVALID_ARGUMENT, "rows and nseg must be >= 1");
+    RF_REQUIRE(nseg <= 1024, RF_ERR_UNSUPPORTED, "nseg must be <= 1024 (got %lld)", (long long)nseg);
+    RF_REQUIRE(D >= 1, RF_ERR_INVALID_ARGUMENT, "D must be >= 1");
+    RF_REQUIRE(D == 64 || D == 128, RF_ERR_UNSUPPORTED, "D must be 64 or 128 (got %lld)", (long long)D);
+    int64_t np, npo, no;
+    RF_REQUIRE(prod({rows, nseg}, &np) && np <= INT32_MAX && prod({np, D}, &npo) && prod({rows, D}, &no) &&
+                   npo < kMaxElems,
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    const uint64_t oes = out_dt == RF_F32 ? 4 : 2;
+    RF_REQUIRE(!overlap(o, no * oes, part_m, np * 4) && !overlap(o, no * oes, part_s, np * 4) &&
+                   !overlap(o, no * oes, part_o, npo * 4) && !overlap(lse, rows * 4, part_m, np * 4) &&
+                   !overlap(lse, rows * 4, part_s, np * 4) && !overlap(lse, rows * 4, part_o, npo * 4) &&
+                   !overlap(lse, rows * 4, o, no * oes),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipError_t e = rf::launch_segment_merge(part_m, part_s, part_o, rows, nseg, int(D), out_dt == RF_BF16, o,
+                                            lse, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_segment_merge launch");
+}
+
+rf_status rf_moe_route(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E,
+                       int64_t k, int32_t* idx, float* w, float* scores, rf_stream stream) {
+    RF_PTR(x, "x");
+    RF_PTR(w_gate, "w_gate");
+    RF_PTR(idx, "idx");
+    RF_PTR(w, "w");
+    RF_OPT_PTR(scores, "scores");
+    RF_REQUIRE(T >= 1 && Hd >= 1 && E >= 1, RF_ERR_INVALID_ARGUMENT, "T, Hd and E must be >= 1");
+    RF_REQUIRE(k >= 1 && k <= E, RF_ERR_INVALID_ARGUMENT, "need 1 <= k <= E (k=%lld, E=%lld)", (long long)k,
+               (long long)E);
+    RF_REQUIRE(Hd % 32 == 0, RF_ERR_UNSUPPORTED, "Hd must be a multiple of 32 (got %lld)", (long long)Hd);
+    RF_REQUIRE(E >= 16 && E <= 256 && E % 16 == 0, RF_ERR_UNSUPPORTED,
+               "E must be a multiple of 16 in [16, 256] (got %lld)", (long long)E);
+    RF_REQUIRE(k <= 8, RF_ERR_UNSUPPORTED, "k must be <= 8 (got %lld)", (long long)k);
+    int64_t nx, ns;
+    RF_REQUIRE(prod({T, Hd}, &nx) && nx < kMaxElems && prod({T, E}, &ns) && T <= INT32_MAX,
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    RF_REQUIRE(!overlap(idx, T * k * 4, x, nx * 2) && !overlap(idx, T * k * 4, w_gate, Hd * E * 2) &&
+                   !overlap(w, T * k * 4, x, nx * 2) && !overlap(w, T * k * 4, w_gate, Hd * E * 2) &&
+                   !overlap(idx, T * k * 4, w, T * k * 4) && !overlap(scores, ns * 4, x, nx * 2) &&
+                   !overlap(scores, ns * 4, w_gate, Hd * E * 2) && !overlap(scores, ns * 4, idx, T * k * 4) &&
+                   !overlap(scores, ns * 4, w, T * k * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipError_t e = rf::launch_moe_route(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate), T,
+                                        Hd, int(E), int(k), idx, w, scores, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_moe_route launch");
+}
+
+size_t rf_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    int64_t n;
+    if (M < 1 || K < 1 || !prod({M, K}, &n)) return 0;
+    return size_t(n);  // the E4M3FN codes of X, when the caller does not ask for them
+}
+
+rf_status rf_quant_gemm(const void* x, const uint8_t* wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, void* y, float* x_scale, uint8_t* xq,
+                        void* workspace, size_t ws_bytes, rf_stream stream) {
+    RF_PTR(x, "x");
+    RF_PTR(wq, "wq");
+    RF_PTR(w_scale, "w_scale");
+    RF_PTR(y, "y");
+    RF_PTR(x_scale, "x_scale");
+    RF_OPT_PTR(xq, "xq");
+    RF_OPT_PTR(workspace, "workspace");
+    RF_REQUIRE(M >= 1 && N >= 1 && K >= 1, RF_ERR_INVALID_ARGUMENT, "M, N and K must be >= 1");
+    RF_REQUIRE(K % 128 == 0, RF_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)K);
+    int64_t nx, nw, ny;
+    RF_REQUIRE(prod({M, K}, &nx) && nx < kMaxElems && prod({N, K}, &nw) && nw < kMaxElems &&
+                   prod({M, N}, &ny) && ny < kMaxElems && M <= INT32_MAX && N <= INT32_MAX,
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    uint8_t* codes = xq;
+    if (!codes) {
+        const size_t need = rf_quant_gemm_workspace_size(M, N, K);
+        RF_REQUIRE(workspace != nullptr && ws_bytes >= need, RF_ERR_BUFFER_TOO_SMALL,
+                   "workspace of %zu bytes needed when xq is NULL (got %zu)", need,
+                   workspace ? ws_bytes : size_t(0));
+        codes = static_cast<uint8_t*>(workspace);
+    }
+    RF_REQUIRE(!overlap(y, ny * 2, x, nx * 2) && !overlap(y, ny * 2, wq, nw) && !overlap(y, ny * 2, w_scale, N * 4) &&
+                   !overlap(x_scale, M * 4, x, nx * 2) && !overlap(x_scale, M * 4, wq, nw) &&
+                   !overlap(x_scale, M * 4, y, ny * 2) && !overlap(x_scale, M * 4, w_scale, N * 4) &&
+                   !overlap(codes, nx, x, nx * 2) && !overlap(codes, nx, wq, nw) && !overlap(codes, nx, y, ny * 2) &&
+                   !overlap(codes, nx, x_scale, M * 4) && !overlap(codes, nx, w_scale, N * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs and workspace must not alias inputs or each other");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rf::launch_quant_rows(static_cast<const uint16_t*>(x), M, K, codes, x_scale, s);
+    if (e != hipSuccess) return device_status(e, "rf_quant_gemm quantise launch");
+    e = rf::launch_fp8_gemm(codes, wq, x_scale, w_scale, M, N, K, static_cast<uint16_t*>(y), s);
+    return device_status(e, "rf_quant_gemm GEMM launch");
+}
+
+}  // extern "C"

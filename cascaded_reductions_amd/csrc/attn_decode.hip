@@ -1,0 +1,219 @@
+// Multi-segment decode attention: the split kernel and the merge kernel.
+//
+// Decode has one query token per (batch, head) row, so the key axis is the only
+// source of parallelism. The Multi-Segment strategy (technical summary
+// "RedFuser: An Automatic Operator Fusion Framework for Cascaded Reductions on AI
+// Accelerators", Methodologie 3; explainer "RedFuser框架：AI加速器中的算子融合技术解析",
+// section 3.3, inter-block merge) splits it into segments reduced independently
+// in the incremental form, then merges the per-segment (max, sum, partial-O)
+// triples with the monoid combination of the fusion conditions (Methodologie 1).
+//
+// Split kernel, one wave per (row, segment). The work is HBM-bound (one FLOP per
+// byte), so it runs on the vector ALUs with 16-byte coalesced loads: a key row of
+// D bf16 values is read by D/8 lanes (8 values each), so one wave load covers
+// 64*8/D consecutive keys ("key slots"). Each key slot keeps its own running
+// (m, s, o~) over the keys it sees; the slots are merged with cross-lane
+// exchanges at the end. Scores are in base-2 units (q pre-scaled by
+// scale * log2 e); the stored maxima are converted back to natural units.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rf {
+namespace {
+
+template <int D, int U>
+__global__ __launch_bounds__(64) void decode_split_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          int64_t L, int64_t nseg, int64_t seglen,
+                                                          float scale_log2, float* __restrict__ part_m,
+                                                          float* __restrict__ part_s,
+                                                          float* __restrict__ part_o) {
+    constexpr int LPK = D / 8;      // lanes per key row
+    constexpr int KPW = 64 / LPK;   // key slots per wave load
+    const int64_t wid = blockIdx.x; // row * nseg + segment
+    const int64_t r = wid / nseg, t = wid - r * nseg;
+    const int lane = threadIdx.x;
+    const int slot = lane / LPK, c = lane % LPK;
+
+    const int64_t a = t * seglen;
+    const int64_t b = a + seglen < L ? a + seglen : L;
+
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    float m = kNegInf, s = 0.f;
+
+    if (a < b) {
+        float qf[8];
+        {
+            const uint4 qr = *reinterpret_cast<const uint4*>(q + r * D + c * 8);
+            const uint32_t w[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qf[2 * i] = bf16_lo(w[i]) * scale_log2;
+                qf[2 * i + 1] = bf16_hi(w[i]) * scale_log2;
+            }
+        }
+        const uint16_t* kr = k + r * L * D + c * 8;
+        const uint16_t* vr = v + r * L * D + c * 8;
+        for (int64_t j0 = a; j0 < b; j0 += KPW * U) {
+            u32x4 kk[U], vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int64_t j = j0 + u * KPW + slot;
+                j = j < b ? j : b - 1;  // masked below; the clamped row is valid
+                kk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + j * D));
+                vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + j * D));
+            }
+            float x[U];
+            float mx = kNegInf;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t w[4] = {kk[u][0], kk[u][1], kk[u][2], kk[u][3]};
+                float dot = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dot = fmaf(qf[2 * i], bf16_lo(w[i]), dot);
+                    dot = fmaf(qf[2 * i + 1], bf16_hi(w[i]), dot);
+                }
+                dot = LPK == 16 ? row16_sum(dot) : row8_sum(dot);
+                x[u] = (j0 + u * KPW + slot < b) ? dot : kNegInf;
+                mx = fmaxf(mx, x[u]);
+            }
+            const float m_new = fmaxf(m, mx);
+            const float m_use = m_new == kNegInf ? 0.f : m_new;
+            const float alpha = exp2_fast(m - m_use);
+            s *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = exp2_fast(x[u] - m_use);
+                s += p;
+                const uint32_t w[4] = {vv[u][0], vv[u][1], vv[u][2], vv[u][3]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[2 * i] = fmaf(p, bf16_lo(w[i]), o[2 * i]);
+                    o[2 * i + 1] = fmaf(p, bf16_hi(w[i]), o[2 * i + 1]);
+                }
+            }
+            m = m_new;
+        }
+        // Merge the key slots: lanes with the same c and different slot.
+#pragma unroll
+        for (int mask = LPK; mask < 64; mask <<= 1) {
+            const float m2 = __shfl_xor(m, mask, 64);
+            const float s2 = __shfl_xor(s, mask, 64);
+            const float M = fmaxf(m, m2);
+            const float w1 = m == kNegInf ? 0.f : exp2_fast(m - M);
+            const float w2 = m2 == kNegInf ? 0.f : exp2_fast(m2 - M);
+            s = w1 * s + w2 * s2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = w1 * o[e] + w2 * __shfl_xor(o[e], mask, 64);
+            m = M;
+        }
+    }
+    if (slot == 0) {
+        float4* dst = reinterpret_cast<float4*>(part_o + wid * D + c * 8);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        if (c == 0) {
+            part_m[wid] = m == kNegInf ? kNegInf : m * kLn2;
+            part_s[wid] = s;
+        }
+    }
+}
+
+// One wave per row; lane owns D/64 output columns.
+template <int D>
+__global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restrict__ part_m,
+                                                            const float* __restrict__ part_s,
+                                                            const float* __restrict__ part_o,
+                                                            int64_t rows, int nseg, int out_bf16,
+                                                            void* __restrict__ out, float* __restrict__ lse) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const float* pm = part_m + r * nseg;
+    const float* ps = part_s + r * nseg;
+    const float* po = part_o + r * nseg * D + lane * PER;
+
+    float M = kNegInf;
+    for (int t = lane; t < nseg; t += 64) M = fmaxf(M, pm[t]);
+    M = wave_max(M);
+    const float M2 = M * kLog2e;
+
+    float S = 0.f, O[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) O[i] = 0.f;
+    for (int t0 = 0; t0 < nseg; t0 += 64) {
+        const int t = t0 + lane;
+        float w = 0.f;
+        if (t < nseg) {
+            const float mt = pm[t];
+            w = mt == kNegInf ? 0.f : exp2_fast(mt * kLog2e - M2);
+            S += w * ps[t];
+        }
+        const int n = nseg - t0 < 64 ? nseg - t0 : 64;
+        for (int tt = 0; tt < n; ++tt) {
+            const float wt = __shfl(w, tt, 64);
+            const float* src = po + int64_t(t0 + tt) * D;
+            if constexpr (PER == 2) {
+                const float2 x = *reinterpret_cast<const float2*>(src);
+                O[0] = fmaf(wt, x.x, O[0]);
+                O[1] = fmaf(wt, x.y, O[1]);
+            } else {
+                O[0] = fmaf(wt, src[0], O[0]);
+            }
+        }
+    }
+    S = wave_sum(S);
+    const bool empty = !(S > 0.f);
+    const float inv = empty ? 0.f : 1.f / S;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const float val = empty ? 0.f : O[i] * inv;
+        const int64_t idx = r * D + lane * PER + i;
+        if (out_bf16)
+            static_cast<uint16_t*>(out)[idx] = uint16_t(f32_to_bf16_rne(val));
+        else
+            static_cast<float*>(out)[idx] = val;
+    }
+    if (lse && lane == 0) lse[r] = empty ? kNegInf : M + __logf(S);
+}
+
+}  // namespace
+
+hipError_t launch_decode_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t R,
+                               int64_t L, int D, int64_t nseg, float scale, float* part_m,
+                               float* part_s, float* part_o, hipStream_t stream) {
+    const int64_t blocks = R * nseg;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t seglen = ceil_div(L, nseg);
+    const float sl2 = scale * kLog2e;
+    if (D == 128)
+        hipLaunchKernelGGL((decode_split_kernel<128, 4>), dim3(unsigned(blocks)), dim3(64), 0, stream, q, k, v, L,
+                           nseg, seglen, sl2, part_m, part_s, part_o);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<64, 4>), dim3(unsigned(blocks)), dim3(64), 0, stream, q, k, v, L,
+                           nseg, seglen, sl2, part_m, part_s, part_o);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_merge(const float* part_m, const float* part_s, const float* part_o,
+                                int64_t rows, int64_t nseg, int D, bool out_bf16, void* o, float* lse,
+                                hipStream_t stream) {
+    const int64_t blocks = ceil_div(rows, 4);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (D == 128)
+        hipLaunchKernelGGL(segment_merge_kernel<128>, dim3(unsigned(blocks)), dim3(256), 0, stream, part_m, part_s,
+                           part_o, rows, int(nseg), int(out_bf16), o, lse);
+    else
+        hipLaunchKernelGGL(segment_merge_kernel<64>, dim3(unsigned(blocks)), dim3(256), 0, stream, part_m, part_s,
+                           part_o, rows, int(nseg), int(out_bf16), o, lse);
+    return hipGetLastError();
+}
+
+}  // namespace rf

@@ -1,0 +1,41 @@
+// Internal launchers: one per kernel family. Each one enqueues its kernel(s)
+// on `stream` and returns hipGetLastError(). Arguments have been validated by
+// the C-ABI layer (abi.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rf {
+
+// Single-segment attention; q/k/v/o are [BH, S, D] row-major.
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                               float* lse, int64_t BH, int64_t Sq, int64_t Sk, int D,
+                               float scale, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* o, float* lse, int64_t BH, int64_t Sq, int64_t Sk,
+                                int D, float scale, hipStream_t stream);
+
+// Multi-segment decode split: q [R, D], k/v [R, L, D] bf16, R = B*H rows.
+hipError_t launch_decode_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               int64_t R, int64_t L, int D, int64_t nseg, float scale,
+                               float* part_m, float* part_s, float* part_o, hipStream_t stream);
+
+// Merge of per-segment partials into o [rows, D] (fp32 or bf16) and lse.
+hipError_t launch_segment_merge(const float* part_m, const float* part_s, const float* part_o,
+                                int64_t rows, int64_t nseg, int D, bool out_bf16, void* o,
+                                float* lse, hipStream_t stream);
+
+// MoE gate: x [T, Hd] bf16, w [Hd, E] bf16 -> idx/w [T, k], optional scores [T, E].
+hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd,
+                            int E, int k, int32_t* idx, float* w, float* scores,
+                            hipStream_t stream);
+
+// Per-row dynamic E4M3FN quantisation of x [M, K] bf16 -> codes [M, K], scale [M].
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes,
+                             float* x_scale, hipStream_t stream);
+// FP8 GEMM with per-row / per-column dequantisation: y[M,N] bf16 = (a[M,K] . b[N,K]^T) * sa[m] * sb[n].
+hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
+                           int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
+}  // namespace rf

@@ -1,0 +1,196 @@
+/*
+ * librf: fused cascaded reductions for AMD Instinct MI355X (gfx950).
+ *
+ * A cascaded reduction is a chain of reductions in which each one depends on
+ * the results of the earlier ones (the safe softmax followed by a GEMM being
+ * the standard case). The library evaluates each chain in a single pass over
+ * its input, keeping only a small running state that is rescaled as new data
+ * arrives (the incremental form), as described on the pages about RedFuser
+ * ("RedFuser: An Automatic Operator Fusion Framework for Cascaded Reductions
+ * on AI Accelerators", ASPLOS 2026): its abstract; the Chinese explainer
+ * "RedFuser框架：AI加速器中的算子融合技术解析" sections 2.2, 2.3, 3.3 and 4.1-4.3;
+ * and the Dutch technical summary ("Technische samenvatting", Methodologie
+ * items 1-3).
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, frees nothing and keeps no pointer after it returns.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL means the
+ *    null stream) and returns; it never synchronises. Results are valid once
+ *    the caller has synchronised with the stream.
+ *  - Sizes are int64_t element counts. Tensors are dense and row-major in the
+ *    layouts stated per call. Every tensor pointer must be 16-byte aligned.
+ *  - Outputs must not alias inputs or each other.
+ *  - Results are deterministic: fixed reduction order, no floating-point atomics.
+ *  - All arguments are validated on the host before any HIP call; an invalid
+ *    call returns an error status, launches nothing and sets rf_last_error().
+ *    A launch failure returns RF_ERR_DEVICE. Faults inside a kernel surface at
+ *    the caller's next synchronisation, as for any HIP kernel.
+ *  - Thread-safe: the only state is a thread-local error message.
+ *  - No call throws across the ABI or aborts the process.
+ */
+#ifndef LIBRF_H
+#define LIBRF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RF_ABI_VERSION 1
+
+/* Exported symbols (the library is built with hidden visibility by default). */
+#if defined(__GNUC__) || defined(__clang__)
+#define RF_API __attribute__((visibility("default")))
+#else
+#define RF_API
+#endif
+
+typedef enum rf_status {
+    RF_OK = 0,
+    RF_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, bad size, misalignment, aliasing  */
+    RF_ERR_UNSUPPORTED = 2,      /* well-formed but outside what this build implements */
+    RF_ERR_BUFFER_TOO_SMALL = 3, /* a caller-provided workspace is too small        */
+    RF_ERR_DEVICE = 4            /* the HIP runtime reported an error              */
+} rf_status;
+
+typedef enum rf_dtype {
+    RF_F32 = 0,  /* IEEE binary32                                   */
+    RF_BF16 = 1  /* bfloat16 (upper half of a binary32), RNE rounding */
+} rf_dtype;
+
+/* A hipStream_t passed as an opaque pointer; NULL is the null stream. */
+typedef void* rf_stream;
+
+/* RF_ABI_VERSION of the loaded library. */
+RF_API int rf_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+RF_API const char* rf_status_string(rf_status s);
+
+/* Detail of the last error on the calling thread ("" if none). The string is
+ * owned by the library and valid until the thread's next librf call. */
+RF_API const char* rf_last_error(void);
+
+/*
+ * rf_softmax_gemm_fused -- single-segment fused attention, O = softmax(scale * Q K^T) V.
+ *
+ * The softmax -> GEMM cascade of the explainer's sections 2.2 and 4.1: the
+ * running maximum, running sum of exponentials and output accumulator of each
+ * query row are updated once per key tile (rescaled by exp(m_old - m_new)),
+ * and O is normalised once at the end. One workgroup owns a block of query
+ * rows and walks the whole key axis (the Single-Segment strategy of the
+ * technical summary, Methodologie 3). Non-causal, no mask.
+ *
+ *   dt     RF_F32 or RF_BF16: the element type of q, k, v and o.
+ *   q      [B, H, Sq, D]   queries.
+ *   k, v   [B, H, Sk, D]   keys and values.
+ *   o      [B, H, Sq, D]   output (written), same dtype as q.
+ *   lse    [B, H, Sq] fp32 natural-log logsumexp of the scaled scores,
+ *          m + ln(s); may be NULL.
+ *   scale  the softmax scale applied to Q K^T before the maximum.
+ *   Supported: B, H, Sq, Sk >= 1; D in {64, 128}; B*H*Sq*D and B*H*Sk*D below 2^40.
+ *   Accumulation is fp32. bf16 outputs are rounded to nearest even.
+ */
+RF_API rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const void* v,
+                                void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
+                                int64_t Sk, int64_t D, float scale, rf_stream stream);
+
+/*
+ * rf_attn_decode_split -- multi-segment decode attention, first kernel of two.
+ *
+ * One query token per (batch, head). The key axis L is split into nseg
+ * contiguous segments of ceil(L/nseg) keys (trailing segments may be shorter
+ * or empty), and each segment is reduced independently in the incremental
+ * form (the Multi-Segment strategy of the technical summary, Methodologie 3;
+ * the inter-block level of the explainer's section 3.3). For segment t of row
+ * r = b*H + h it writes
+ *     part_m[r*nseg + t]        = max_j x_j over the segment           (or -inf if empty)
+ *     part_s[r*nseg + t]        = sum_j exp(x_j - part_m)              (or 0)
+ *     part_o[(r*nseg + t)*D + d] = sum_j exp(x_j - part_m) v_j[d]     (or 0), unnormalised,
+ * with x_j = scale * <q, k_j>. Combine the partials with rf_segment_merge.
+ *
+ *   q        [B, H, D] bf16.     k, v  [B, H, L, D] bf16.
+ *   part_m, part_s  fp32, B*H*nseg elements each.  part_o  fp32, B*H*nseg*D elements.
+ *   Supported: B, H >= 1; 1 <= nseg <= L; D in {64, 128}; B*H*nseg <= 2^31 - 1.
+ */
+RF_API rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int64_t B,
+                               int64_t H, int64_t L, int64_t D, int64_t nseg, float scale,
+                               float* part_m, float* part_s, float* part_o, rf_stream stream);
+
+/*
+ * rf_segment_merge -- merge of per-segment (max, sum, partial-O) triples.
+ *
+ * For each row r: m = max_t part_m, w_t = exp(part_m[t] - m) (0 for a segment
+ * whose maximum is -inf), s = sum_t w_t part_s[t], o = sum_t w_t part_o[t] / s,
+ * lse = m + ln(s). This is the commutative-monoid combination that the fusion
+ * conditions of the technical summary (Methodologie 1) make exact; a row whose
+ * segments are all empty gives o = 0 and lse = -inf.
+ *
+ *   part_m, part_s  [rows, nseg] fp32.  part_o  [rows, nseg, D] fp32.
+ *   out_dt  RF_F32 or RF_BF16 (RNE): the dtype of o.   o  [rows, D].
+ *   lse     [rows] fp32, may be NULL.
+ *   Supported: rows >= 1, 1 <= nseg <= 1024, D in {64, 128}.
+ */
+RF_API rf_status rf_segment_merge(const float* part_m, const float* part_s, const float* part_o,
+                           int64_t rows, int64_t nseg, int64_t D, rf_dtype out_dt, void* o,
+                           float* lse, rf_stream stream);
+
+/*
+ * rf_moe_route -- fused MoE gate: scores = X W_gate -> top-k -> softmax over the k.
+ *
+ * The cascade of the explainer's section 4.2 in one kernel; the score matrix
+ * never reaches memory (unless the optional debug output is requested).
+ * Experts are ordered by descending score, equal scores by the lower expert
+ * index. The weights are the softmax of the k selected scores:
+ * w_r = exp(s_r - s_1) / sum_r' exp(s_r' - s_1). Scores accumulate in fp32.
+ *
+ *   x       [T, Hd] bf16 tokens.   w_gate  [Hd, E] bf16 (expert index contiguous).
+ *   idx     [T, k] int32 expert indices.   w  [T, k] fp32 weights.
+ *   scores  [T, E] fp32 debug copy of the gate scores, or NULL.
+ *   Supported: T >= 1; Hd >= 32 and Hd % 32 == 0; 16 <= E <= 256 and E % 16 == 0;
+ *   1 <= k <= min(8, E).
+ */
+RF_API rf_status rf_moe_route(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E,
+                       int64_t k, int32_t* idx, float* w, float* scores, rf_stream stream);
+
+/*
+ * rf_quant_gemm_workspace_size -- bytes of device workspace rf_quant_gemm needs
+ * for this shape when xq is NULL (0 when it needs none). With xq non-NULL no
+ * workspace is needed.
+ */
+RF_API size_t rf_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * rf_quant_gemm -- dynamic per-row FP8 quantisation fused with an FP8 GEMM.
+ *
+ * The cascade of the explainer's section 4.3 with one scale per row of X:
+ *     a_i      = max_k |x_ik|
+ *     sigma_i  = fl32(a_i / 448)                (x_scale[i], IEEE fp32 division)
+ *     c_ik     = E4M3FN_RNE(fl32(x_ik / sigma_i))  (OCP FP8 E4M3FN, ties to even,
+ *                                                  sign of zero kept; all 0 if a_i = 0)
+ *     y_ij     = bf16_RNE(sigma_i * w_scale_j * sum_k dec(c_ik) dec(wq_jk))
+ * The sum is accumulated in fp32 on the FP8 matrix cores.
+ *
+ *   x        [M, K] bf16.
+ *   wq       [N, K] E4M3FN codes: row j holds column j of the K x N weight.
+ *   w_scale  [N] fp32 per-column weight scale.
+ *   y        [M, N] bf16 output.   x_scale [M] fp32 output (required).
+ *   xq       [M, K] E4M3FN codes output, or NULL.
+ *   workspace, ws_bytes  device scratch of at least
+ *            rf_quant_gemm_workspace_size(M, N, K) bytes when xq is NULL
+ *            (RF_ERR_BUFFER_TOO_SMALL otherwise); may be NULL when that is 0.
+ *   Supported: M, N >= 1; K >= 128 and K % 128 == 0; M*K, N*K, M*N below 2^40.
+ */
+RF_API rf_status rf_quant_gemm(const void* x, const uint8_t* wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, void* y, float* x_scale, uint8_t* xq,
+                        void* workspace, size_t ws_bytes, rf_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRF_H */

@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports every symbol include/librf.h declares, and
+rejects invalid arguments on the host (no GPU needed: validation runs before
+any HIP call, and no call here passes validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import cascaded_reductions_amd as rf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "librf.h")
+
+OK, INVALID, UNSUPPORTED, TOO_SMALL, DEVICE = 0, 1, 2, 3, 4
+P = 0x100000  # a fake, 16-byte aligned device address; never dereferenced
+P2, P3, P4, P5, P6 = (P * i for i in range(2, 7))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^RF_API\s+[\w\s\*]+?\b(rf_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rf.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted([
+        "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused",
+        "rf_attn_decode_split", "rf_segment_merge", "rf_moe_route", "rf_quant_gemm_workspace_size",
+        "rf_quant_gemm"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rf_abi_version() == 1
+    for code, name in [(0, b"RF_OK"), (1, b"RF_ERR_INVALID_ARGUMENT"), (2, b"RF_ERR_UNSUPPORTED"),
+                       (3, b"RF_ERR_BUFFER_TOO_SMALL"), (4, b"RF_ERR_DEVICE")]:
+        assert lib.rf_status_string(code) == name
+    assert lib.rf_status_string(99) == b"RF_STATUS_UNKNOWN"
+
+
+def _attn(lib, dt=0, q=P, k=P2, v=P3, o=P4, lse=None, B=1, H=1, Sq=4, Sk=4, D=64, scale=0.125):
+    return lib.rf_softmax_gemm_fused(dt, q, k, v, o, lse, B, H, Sq, Sk, D, scale, None)
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, dt=7) == INVALID
+    assert _attn(lib, q=None) == INVALID
+    assert b"q must not be NULL" in lib.rf_last_error()
+    assert _attn(lib, k=P2 + 8) == INVALID
+    assert b"aligned" in lib.rf_last_error()
+    assert _attn(lib, lse=P5 + 4) == INVALID
+    assert _attn(lib, Sq=0) == INVALID
+    assert _attn(lib, Sk=-1) == INVALID
+    assert _attn(lib, D=0) == INVALID
+    assert _attn(lib, D=96) == UNSUPPORTED
+    assert _attn(lib, D=256) == UNSUPPORTED
+    assert _attn(lib, scale=float("inf")) == INVALID
+    assert _attn(lib, scale=float("nan")) == INVALID
+    assert _attn(lib, o=P) == INVALID                       # output aliases q
+    assert _attn(lib, lse=P4 + 64) == INVALID               # lse inside o
+    assert _attn(lib, B=1 << 40, H=1 << 30) == UNSUPPORTED  # overflow guarded
+
+
+def _split(lib, q=P, k=P2, v=P3, B=2, H=2, L=64, D=128, nseg=8, pm=P4, ps=P5, po=P6):
+    return lib.rf_attn_decode_split(q, k, v, B, H, L, D, nseg, 0.088, pm, ps, po, None)
+
+
+def test_decode_split_validation(lib):
+    assert _split(lib, q=None) == INVALID
+    assert _split(lib, pm=None) == INVALID
+    assert _split(lib, nseg=0) == INVALID
+    assert _split(lib, nseg=65) == INVALID
+    assert b"nseg" in lib.rf_last_error()
+    assert _split(lib, L=0) == INVALID
+    assert _split(lib, D=80) == UNSUPPORTED
+    assert _split(lib, pm=P5) == INVALID                    # part_m aliases part_s
+
+
+def _merge(lib, pm=P, ps=P2, po=P3, rows=4, nseg=8, D=128, dt=1, o=P4, lse=None):
+    return lib.rf_segment_merge(pm, ps, po, rows, nseg, D, dt, o, lse, None)
+
+
+def test_merge_validation(lib):
+    assert _merge(lib, po=None) == INVALID
+    assert _merge(lib, dt=5) == INVALID
+    assert _merge(lib, rows=0) == INVALID
+    assert _merge(lib, nseg=0) == INVALID
+    assert _merge(lib, nseg=2048) == UNSUPPORTED
+    assert _merge(lib, D=32) == UNSUPPORTED
+    assert _merge(lib, o=P3) == INVALID
+    assert _merge(lib, lse=P4 + 16) == INVALID
+
+
+def _moe(lib, x=P, w=P2, T=8, Hd=64, E=64, k=2, idx=P3, wt=P4, sc=None):
+    return lib.rf_moe_route(x, w, T, Hd, E, k, idx, wt, sc, None)
+
+
+def test_moe_validation(lib):
+    assert _moe(lib, x=None) == INVALID
+    assert _moe(lib, k=0) == INVALID
+    assert _moe(lib, k=65) == INVALID
+    assert _moe(lib, k=9) == UNSUPPORTED
+    assert _moe(lib, Hd=48) == UNSUPPORTED
+    assert _moe(lib, E=40) == UNSUPPORTED
+    assert _moe(lib, E=512) == UNSUPPORTED
+    assert _moe(lib, T=0) == INVALID
+    assert _moe(lib, idx=P4) == INVALID                     # idx aliases w
+    assert _moe(lib, sc=P + 16) == INVALID                  # scores inside x
+
+
+def _qg(lib, x=P, wq=P2, ws=P3, M=16, N=16, K=256, y=P4, xs=P5, xq=P6, work=None, nbytes=0):
+    return lib.rf_quant_gemm(x, wq, ws, M, N, K, y, xs, xq, work, nbytes, None)
+
+
+def test_quant_gemm_validation(lib):
+    assert lib.rf_quant_gemm_workspace_size(16, 16, 256) == 16 * 256
+    assert lib.rf_quant_gemm_workspace_size(0, 16, 256) == 0
+    assert _qg(lib, x=None) == INVALID
+    assert _qg(lib, xs=None) == INVALID
+    assert _qg(lib, K=100) == UNSUPPORTED
+    assert _qg(lib, M=0) == INVALID
+    assert _qg(lib, xq=None) == TOO_SMALL
+    assert _qg(lib, xq=None, work=P6, nbytes=16 * 256 - 1) == TOO_SMALL
+    assert _qg(lib, y=P) == INVALID
+    assert _qg(lib, xq=P4 + 16) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rf.softmax_gemm_fused(q, q, q)
