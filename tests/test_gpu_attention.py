@@ -59,3 +59,54 @@ def test_f32_deterministic(rf):
     o1, l1 = _run(rf, inp)
     o2, l2 = _run(rf, inp)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------------ bf16 (matrix cores)
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,scale", [
+    (1, 2, 64, 64, 64, 0.125),        # one tile
+    (2, 3, 100, 300, 64, 0.125),      # ragged queries and keys, several tiles
+    (1, 1, 1, 1, 64, 0.125),          # one query, one key
+    (1, 2, 130, 65, 64, 1.0),         # key tail of one, large scores
+    (2, 2, 77, 200, 128, 0.0883883),  # D = 128
+    (1, 1, 40, 1000, 64, 3.0),        # scores up to ~50: the reference maximum must move
+    (1, 1, 64, 128, 64, -0.125),      # negative scale
+    (1, 1, 64, 96, 64, 0.0),          # scale 0: the mean of V
+])
+def test_bf16_shapes(rf, B, H, Sq, Sk, D, scale):
+    inp = attn_inputs(B, H, Sq, Sk, D, "bf16", seed=500 + Sq + Sk, scale=scale)
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+def test_bf16_growing_scores(rf):
+    """Keys whose scores grow along the key axis force a rescale on every tile."""
+    inp = attn_inputs(1, 2, 64, 640, 64, "bf16", seed=21, scale=0.125)
+    from synth import f32_to_bf16_bits
+    kf = bf16_bits_to_f32(inp.k) + np.linspace(0, 12, 640, dtype=np.float32)[None, None, :, None] * \
+        np.sign(bf16_bits_to_f32(inp.q).mean(axis=2, keepdims=True))
+    inp.k = f32_to_bf16_bits(kf.astype(np.float32))
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+def test_bf16_bert_workload(rf):
+    """The BERT-base prefill shape: 8 x 12 heads, 512 x 512, D = 64, every output checked."""
+    c = CONFIGS["C2"]
+    inp = attn_inputs(c["B"], c["H"], c["Sq"], c["Sk"], c["D"], "bf16", c["seed"], c["scale"])
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+def test_bf16_deterministic(rf):
+    inp = attn_inputs(2, 2, 100, 300, 64, "bf16", seed=8)
+    o1, l1 = _run(rf, inp)
+    o2, l2 = _run(rf, inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
