@@ -15,7 +15,7 @@ import os
 __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16",
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode",
-    "moe_route", "quant_gemm", "quant_gemm_workspace_size",
+    "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +44,8 @@ _SIGS = {
     "rf_softmax_gemm_fused": ([_c.c_int, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P], _c.c_int),
     "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
-    "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
+    "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_quant_gemm": ([_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
 }
@@ -187,7 +188,27 @@ def attn_decode(q, k, v, nseg: int, scale: float | None = None, out_dtype=None):
 # ------------------------------------------------------------------ MoE gate
 
 
-def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False):
+def moe_route_workspace_size(T: int, Hd: int, E: int) -> int:
+    return int(load().rf_moe_route_workspace_size(T, Hd, E))
+
+
+_moe_ws = {}
+
+
+def _moe_workspace(device, nbytes):
+    """A zero-filled workspace per device, grown on demand. The library leaves its
+    counters at zero after every call, so the buffer can be reused; calls that
+    share it must be ordered (same stream), as with any scratch buffer."""
+    torch = _torch()
+    key = (device.type, device.index)
+    ws = _moe_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _moe_ws[key] = ws
+    return ws
+
+
+def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False, workspace=None):
     """x [T,Hd] bf16, w_gate [Hd,E] bf16 -> (idx [T,k] int32, w [T,k] fp32, scores [T,E] fp32 or None)."""
     torch = _torch()
     T, Hd = x.shape
@@ -202,7 +223,12 @@ def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores
         scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
     if scores is not None:
         _need(scores, "scores", torch.float32, (T, E))
-    _check(load().rf_moe_route(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores), _stream(x)))
+    need = moe_route_workspace_size(T, Hd, E)
+    if workspace is None:
+        workspace = _moe_workspace(x.device, need)
+    _need(workspace, "workspace", torch.uint8)
+    _check(load().rf_moe_route(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores),
+                               _ptr(workspace), workspace.numel(), _stream(x)))
     return idx, w, scores
 
 

@@ -27,8 +27,10 @@ hipError_t launch_segment_merge(const float* part_m, const float* part_s, const 
                                 float* lse, hipStream_t stream);
 
 // MoE gate: x [T, Hd] bf16, w [Hd, E] bf16 -> idx/w [T, k], optional scores [T, E].
+// The workspace holds per-token-block counters and partial score blocks.
+size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E);
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd,
-                            int E, int k, int32_t* idx, float* w, float* scores,
+                            int E, int k, int32_t* idx, float* w, float* scores, void* workspace,
                             hipStream_t stream);
 
 // Per-row dynamic E4M3FN quantisation of x [M, K] bf16 -> codes [M, K], scale [M].

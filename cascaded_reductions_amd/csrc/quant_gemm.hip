@@ -1,0 +1,260 @@
+// Dynamic FP8 quantisation fused with an FP8 GEMM.
+//
+// The cascade of the explainer "RedFuser框架：AI加速器中的算子融合技术解析",
+// section 4.3: scale = max|X| / 448 per row, codes = round(X / scale) to OCP
+// E4M3FN, then Y = codes . W dequantised by the row and column scales. The
+// scale needs the whole row's maximum before any code can be formed, and
+// rounding has no incremental form (its inverse does not exist), so the cascade
+// runs as two launches on one stream (the explainer's multi-kernel level,
+// section 3.3):
+//  1. quant_rows: one workgroup per row keeps the row in registers, reduces the
+//     absolute maximum (an integer max over the bf16 magnitude bits), forms
+//     sigma = a / 448 and each code from the IEEE fp32 quotient x / sigma with
+//     the hardware round-to-nearest-even E4M3FN conversion (v_cvt_pk_fp8_f32,
+//     which keeps the sign of zero and saturates at 448);
+//  2. fp8_gemm: 256 x 256 output tiles, 8 waves, K steps of 128 code bytes
+//     double buffered in LDS (filled by direct global-to-LDS loads, so no
+//     registers are spent on staging). Both operands are K-contiguous, so no
+//     transposes are needed. The product is formed as C^T = W X^T so that every
+//     lane ends with four consecutive output columns of one row; the epilogue
+//     applies (acc * sigma_i) * w_scale_j and rounds to bf16.
+//
+// Accumulation precision. The product must be accumulated in fp32. gfx950's
+// FP8 matrix instructions (v_mfma_scale_f32_*_f8f6f4 and v_mfma_f32_*_fp8_fp8)
+// align the products of one instruction to the largest of them and keep only
+// 13 bits below it (measured: 2^16 + 2^3 is kept, 2^16 + 2^2 is lost), which on
+// rows with x20 outliers leaves near-cancelling outputs visibly wrong. The
+// codes are therefore converted exactly to bf16 in registers after the LDS read
+// and multiplied on v_mfma_f32_32x32x16_bf16, whose accumulation keeps fp32
+// precision (2^16 + 2^-6 is kept). Operands stay 8-bit in HBM and LDS.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rf {
+namespace {
+
+// ------------------------------------------------------------------ 1. per-row quantisation
+
+constexpr int QT = 256;   // threads per row
+constexpr int QC = 4;     // 16-byte chunks kept in registers per thread (rows up to 8192)
+
+__device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+    return uint32_t(v);
+}
+
+__global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ xs) {
+    __shared__ uint32_t sm_max[QT / 64];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* xr = x + row * K;
+    uint8_t* cr = codes + row * K;
+    const int nch = int(K / 8);
+    const bool cached = nch <= QT * QC;
+
+    u32x4 v[QC];
+    uint32_t amax = 0;   // max of the bf16 magnitude bits: ordered like the magnitudes
+    for (int i = 0; i < (nch + QT - 1) / QT; ++i) {
+        const int ch = tid + i * QT;
+        if (ch >= nch) break;
+        const u32x4 t = *reinterpret_cast<const u32x4*>(xr + ch * 8);
+        if (i < QC) v[i] = t;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            amax = max(amax, t[w] & 0x7FFFu);
+            amax = max(amax, (t[w] >> 16) & 0x7FFFu);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = max(amax, uint32_t(__shfl_xor(int(amax), m, 64)));
+    if ((tid & 63) == 0) sm_max[tid >> 6] = amax;
+    __syncthreads();
+    amax = sm_max[0];
+#pragma unroll
+    for (int w = 1; w < QT / 64; ++w) amax = max(amax, sm_max[w]);
+
+    const float a = bf16_to_f32(amax);
+    const float sigma = a / 448.0f;      // IEEE fp32 division
+    if (tid == 0) xs[row] = sigma;
+
+    for (int i = 0; i < (nch + QT - 1) / QT; ++i) {
+        const int ch = tid + i * QT;
+        if (ch >= nch) break;
+        const u32x4 t = (cached && i < QC) ? v[i] : *reinterpret_cast<const u32x4*>(xr + ch * 8);
+        uint32_t out[2] = {0u, 0u};
+        if (sigma > 0.f) {
+            float q[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                q[2 * w] = bf16_lo(t[w]) / sigma;       // IEEE fp32 quotient
+                q[2 * w + 1] = bf16_hi(t[w]) / sigma;
+            }
+            out[0] = codes4(q[0], q[1], q[2], q[3]);
+            out[1] = codes4(q[4], q[5], q[6], q[7]);
+        }
+        *reinterpret_cast<uint2*>(cr + ch * 8) = make_uint2(out[0], out[1]);
+    }
+}
+
+// ------------------------------------------------------------------ 2. FP8 GEMM
+
+constexpr int BT = 256;        // tile rows (N) and columns (M)
+constexpr int BK = 128;        // bytes of K per step
+constexpr int GW = 8;          // waves
+constexpr int GT = GW * 64;    // threads
+constexpr int TILE_BYTES = BT * BK;                     // 32 KiB per operand per stage
+
+// Eight E4M3FN codes (two dwords) -> eight bf16 values. Every E4M3FN value is exactly
+// representable in bf16, so the conversion (v_cvt_scalef32_pk_bf16_fp8, scale 1) is exact.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    const u32x4 u = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                     __builtin_bit_cast(uint32_t, d)};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// LDS row of 128 bytes = 8 chunks of 16 bytes, chunk index XOR-swizzled by row.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq,
+                                                      const float* __restrict__ xs, const float* __restrict__ ws,
+                                                      int64_t M, int64_t N, int64_t K, int tiles_m,
+                                                      uint16_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILE_BYTES];   // [stage][W, X]
+
+    // Tile order: XCD-major so that the tiles one XCD runs share operand rows in its L2.
+    int64_t bid = blockIdx.x;
+    const int64_t total = int64_t(gridDim.x);
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int64_t tn = bid / tiles_m, tm = bid - tn * tiles_m;
+    const int64_t n0 = tn * BT, m0 = tm * BT;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int wn = wave >> 2;      // 0..1 : 128 rows of N each
+    const int wm = wave & 3;       // 0..3 : 64 columns of M each
+
+    // Global -> LDS without registers (global_load_lds_dwordx4): one wave instruction
+    // fills 1 KiB of LDS = 8 rows of 128 bytes, lane i landing in row i/8, physical
+    // chunk i%8; the lane therefore fetches logical chunk (i%8) ^ (row & 7).
+    // Waves 0-3 fill the W tile, waves 4-7 the X tile, 8 instructions each.
+    const int which = wave >> 2;
+    const uint8_t* gsrc = which ? xq : wq;
+    const int64_t lim = which ? M : N;
+    const int64_t base_row = which ? m0 : n0;
+    auto load = [&](int64_t k0, int st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r0 = ((wave & 3) * 8 + j) * 8;
+            const int r = r0 + (lane >> 3);
+            const int ch = (lane & 7) ^ (r & 7);
+            int64_t gr = base_row + r;
+            gr = gr < lim ? gr : lim - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(gsrc + gr * K + k0 + ch * 16),
+                (__attribute__((address_space(3))) void*)(&smem[st][which][r0 * BK]), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+    const int64_t nk = K / BK;
+    load(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int64_t t = 0; t < nk; ++t) {
+        const int st = int(t & 1);
+        if (t + 1 < nk) load((t + 1) * BK, st ^ 1);
+        const uint8_t* sw = smem[st][0];
+        const uint8_t* sx = smem[st][1];
+#pragma unroll
+        for (int p = 0; p < BK / 32; ++p) {
+            // Lane (row l32, half g) reads the 16 code bytes [32p + 16g, +16) of its row and
+            // converts them exactly to bf16: bytes 0-7 feed the first K=16 MFMA of the pair,
+            // bytes 8-15 the second (the same slot-to-k map for both operands).
+            bf16x8 alo[4], ahi[4], blo[2], bhi[2];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int r = wn * 128 + a * 32 + l32;
+                const u32x4 raw = *reinterpret_cast<const u32x4*>(sw + swz(r, 2 * p + g));
+                alo[a] = fp8x8_to_bf16(raw[0], raw[1]);
+                ahi[a] = fp8x8_to_bf16(raw[2], raw[3]);
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int r = wm * 64 + b * 32 + l32;
+                const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + swz(r, 2 * p + g));
+                blo[b] = fp8x8_to_bf16(raw[0], raw[1]);
+                bhi[b] = fp8x8_to_bf16(raw[2], raw[3]);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[a], blo[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[a], bhi[b], acc[a][b], 0, 0, 0);
+                }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    // acc[a][b][r] = C^T[n][m]: n = n0 + wn*128 + a*32 + (r/4)*8 + 4g + r%4, m = m0 + wm*64 + b*32 + l32.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t m = m0 + wm * 64 + b * 32 + l32;
+        if (m >= M) continue;
+        const float sx = xs[m];
+        uint16_t* yr = y + m * N;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int64_t n = n0 + wn * 128 + a * 32 + q4 * 8 + 4 * g;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t nn = n + e < N ? n + e : N - 1;
+                    v[e] = (acc[a][b][4 * q4 + e] * sx) * ws[nn];
+                }
+                if (n + 3 < N) {
+                    *reinterpret_cast<uint2*>(yr + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[n + e] = uint16_t(f32_to_bf16_rne(v[e]));
+                }
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, float* x_scale,
+                             hipStream_t stream) {
+    if (M > INT32_MAX || K / 8 > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(M)), dim3(QT), 0, stream, x, K, codes, x_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb, int64_t M,
+                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    const int64_t tm = ceil_div(M, BT), tn = ceil_div(N, BT);
+    const int64_t blocks = tm * tn;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_gemm_kernel, dim3(unsigned(blocks)), dim3(GT), 0, stream, a, b, sa, sb, M, N, K, int(tm),
+                       y);
+    return hipGetLastError();
+}
+
+}  // namespace rf

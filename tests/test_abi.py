@@ -30,8 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused",
-        "rf_attn_decode_split", "rf_segment_merge", "rf_moe_route", "rf_quant_gemm_workspace_size",
-        "rf_quant_gemm"])
+        "rf_attn_decode_split", "rf_segment_merge", "rf_moe_route_workspace_size", "rf_moe_route",
+        "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -101,8 +101,8 @@ def test_merge_validation(lib):
     assert _merge(lib, lse=P4 + 16) == INVALID
 
 
-def _moe(lib, x=P, w=P2, T=8, Hd=64, E=64, k=2, idx=P3, wt=P4, sc=None):
-    return lib.rf_moe_route(x, w, T, Hd, E, k, idx, wt, sc, None)
+def _moe(lib, x=P, w=P2, T=8, Hd=64, E=64, k=2, idx=P3, wt=P4, sc=None, ws=P6, nbytes=1 << 20):
+    return lib.rf_moe_route(x, w, T, Hd, E, k, idx, wt, sc, ws, nbytes, None)
 
 
 def test_moe_validation(lib):
@@ -116,6 +116,11 @@ def test_moe_validation(lib):
     assert _moe(lib, T=0) == INVALID
     assert _moe(lib, idx=P4) == INVALID                     # idx aliases w
     assert _moe(lib, sc=P + 16) == INVALID                  # scores inside x
+    need = lib.rf_moe_route_workspace_size(2048, 4096, 64)
+    assert need == 256 + 32 * 8 * 64 * 64 * 4              # counters + 8 hidden ranges of partial scores
+    assert _moe(lib, ws=None) == TOO_SMALL
+    assert _moe(lib, nbytes=lib.rf_moe_route_workspace_size(8, 64, 64) - 1) == TOO_SMALL
+    assert _moe(lib, ws=P + 64) == INVALID                  # workspace inside x
 
 
 def _qg(lib, x=P, wq=P2, ws=P3, M=16, N=16, K=256, y=P4, xs=P5, xq=P6, work=None, nbytes=0):

@@ -1,0 +1,121 @@
+"""GPU parity: rf_quant_gemm against the oracle (absmax -> scale -> round -> GEMM).
+
+Row scales and E4M3FN codes must be bit-exact; Y is compared within the bf16
+tolerance (the oracle accumulates exactly in fp64, the GPU in fp32 on the
+matrix cores and rounds Y to bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, quant_inputs
+from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_u8, host
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-2, 1e-2
+
+
+def _check(rf, x, wq, ws, use_workspace=False):
+    dx, dwq, dws = dev_bf16(x), dev_u8(wq), dev_f32(ws)
+    if use_workspace:
+        y, xs, _ = rf.quant_gemm(dx, dwq, dws)
+        codes = None
+    else:
+        y, xs, codes = rf.quant_gemm(dx, dwq, dws, return_codes=True)
+    torch.cuda.synchronize()
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    ry, rsig, rcodes = oracle.quant_gemm(xf, wq, ws)
+    np.testing.assert_array_equal(host(xs).astype(np.float32), rsig.astype(np.float32))
+    if codes is not None:
+        gc = codes.cpu().numpy()
+        bad = np.argwhere(gc != rcodes)
+        assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: got {gc[tuple(bad[0])]:#x} " \
+                              f"want {rcodes[tuple(bad[0])]:#x} (x={xf[tuple(bad[0])]!r})"
+    assert_close(host(y), ry, ATOL, RTOL, "Y")
+    return host(y)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (5, 7, 128),          # far below one tile
+    (100, 300, 256),      # ragged tiles in both directions
+    (256, 256, 512),      # exactly one tile
+    (1, 1, 128),
+    (300, 520, 1024),
+    (513, 257, 384),
+])
+def test_quant_gemm_shapes(rf, M, N, K):
+    x, wq, ws = quant_inputs(M, N, K, seed=700 + M + N + K)
+    _check(rf, x, wq, ws)
+
+
+def test_zero_and_tiny_rows(rf):
+    x, wq, ws = quant_inputs(40, 64, 256, seed=71)
+    xf = bf16_bits_to_f32(x).copy()
+    xf[3] = 0.0                                         # zero row: scale 0, codes 0, Y row 0
+    xf[5] = xf[5] * np.float32(1e-30)                   # tiny magnitudes (subnormal-range quotients avoided)
+    xf[7, :] = 0.0
+    xf[7, 10] = -2.0                                    # a single nonzero: every other code is +0
+    xf[9] = np.where(np.arange(256) % 2 == 0, 1e-3, -1e-3).astype(np.float32)
+    xf[9, 0] = 40.0                                     # many values that round to +-0 (codes 0x00 / 0x80)
+    x = f32_to_bf16_bits(xf.astype(np.float32))
+    y = _check(rf, x, wq, ws)
+    assert np.all(y[3] == 0)
+
+
+def test_workspace_path_matches(rf):
+    x, wq, ws = quant_inputs(130, 200, 512, seed=72)
+    a = _check(rf, x, wq, ws, use_workspace=False)
+    b = _check(rf, x, wq, ws, use_workspace=True)
+    assert np.array_equal(a, b)
+
+
+def test_identity_weight(rf):
+    """W = I (codes 0x38 = 1.0 on the diagonal, unit scales): Y = sigma_i * dec(c_ik)."""
+    x, _, _ = quant_inputs(64, 256, 256, seed=73)
+    wq = np.zeros((256, 256), np.uint8)
+    np.fill_diagonal(wq, 0x38)
+    _check(rf, x, wq, np.ones(256, np.float32))
+
+
+@pytest.mark.slow
+def test_quant_gemm_workload(rf):
+    """The 4096^3 workload: every scale, every code and every output element checked."""
+    c = CONFIGS["C5"]
+    x, wq, ws = quant_inputs(c["M"], c["N"], c["K"], c["seed"])
+    _check(rf, x, wq, ws)
+
+
+def _all_finite_codes():
+    c = np.arange(256, dtype=np.uint8)
+    return c[(c & 0x7F) != 0x7F]                       # 254 codes: both zeros, subnormals, normals
+
+
+def test_every_code_through_the_activation_operand(rf):
+    """X row 0 holds every finite E4M3FN value (absmax 448, so sigma = 1 and the codes
+    are the values themselves); with W = I, Y row 0 must equal those values exactly."""
+    codes = _all_finite_codes()
+    vals = oracle.e4m3fn_decode(codes)
+    K = 256
+    xf = np.zeros((2, K), np.float32)
+    xf[0, :codes.size] = vals
+    xf[1, 0] = 1.0
+    x = f32_to_bf16_bits(xf)
+    wq = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(wq, 0x38)
+    y = _check(rf, x, wq, np.ones(K, np.float32))
+    np.testing.assert_array_equal(y[0, :codes.size], vals)
+
+
+def test_every_code_through_the_weight_operand(rf):
+    """X = 448 I (each row's only nonzero is 448: sigma = 1, code 0x7E); W column j holds
+    every finite code, so Y = 448 * dec(code), exact in bf16."""
+    codes = _all_finite_codes()
+    K = 256
+    x = f32_to_bf16_bits((np.eye(K, dtype=np.float32) * 448.0))
+    wq = np.zeros((4, K), np.uint8)
+    wq[0, :codes.size] = codes
+    wq[1, :codes.size] = codes[::-1]
+    y = _check(rf, x, wq, np.ones(4, np.float32))
+    np.testing.assert_array_equal(y[:codes.size, 0], 448.0 * oracle.e4m3fn_decode(codes))
+    np.testing.assert_array_equal(y[:codes.size, 1], 448.0 * oracle.e4m3fn_decode(codes[::-1]))
