@@ -196,14 +196,13 @@ _moe_ws = {}
 
 
 def _moe_workspace(device, nbytes):
-    """A zero-filled workspace per device, grown on demand. The library leaves its
-    counters at zero after every call, so the buffer can be reused; calls that
-    share it must be ordered (same stream), as with any scratch buffer."""
+    """A workspace per device, grown on demand; calls that share it must be ordered
+    (same stream), as with any scratch buffer."""
     torch = _torch()
     key = (device.type, device.index)
     ws = _moe_ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         _moe_ws[key] = ws
     return ws
 

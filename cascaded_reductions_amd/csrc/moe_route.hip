@@ -1,8 +1,8 @@
 // Fused MoE gate: scores = X W_gate -> top-k -> softmax over the k selected.
 //
 // The cascade of the explainer "RedFuser框架：AI加速器中的算子融合技术解析",
-// section 4.2, in one launch; the score matrix is never written (except as an
-// optional debug output).
+// section 4.2; the full score matrix is never written (except as an optional
+// debug output).
 //
 // The gate GEMM reads X once (16.8 MB at 2048 x 4096) but every token needs the
 // whole W_gate, so a kernel that gives each workgroup a few tokens and all of
@@ -15,11 +15,14 @@
 //    (v_mfma_f32_16x16x32_bf16; W enters through the transposing LDS read, so
 //    the [Hd, E] layout needs no transpose in memory), and writes a 64 x E
 //    partial score block to the workspace;
-//  * the last workgroup to finish a token block (a per-block counter) adds the
-//    partial blocks in range order -- a fixed order, so results are
-//    deterministic -- and runs the top-k and the softmax in registers: four
-//    lanes per token each keep a sorted top-k list over a quarter of the
-//    experts, merged with two cross-lane steps. It then resets the counter.
+//  * a second launch adds each token's range partials in range order -- a fixed
+//    order, so results are deterministic -- and runs the top-k and the softmax
+//    in registers: four lanes per token each keep a sorted top-k list over a
+//    quarter of the experts, merged with two cross-lane steps. (Publishing the
+//    partials inside one launch would need an agent-scope release per
+//    workgroup, which on gfx950 writes back the whole L2 of the XCD; the
+//    kernel boundary orders the two phases instead -- the explainer's
+//    multi-kernel level, section 3.3.)
 // Experts are ranked by (score descending, index ascending).
 #include "common.hpp"
 #include "launch.hpp"
@@ -36,18 +39,18 @@ constexpr int kLdsElems = 32768;      // W slice capacity (bf16 elements, 64 KiB
 struct MoeGeom {
     int64_t ntb, nranges;
     int hr;
-    size_t cnt_bytes, part_bytes;
+    size_t part_bytes;
 };
+
+// Width of the hidden range one workgroup reduces: as wide as the 64 KiB LDS slice
+// allows, at most 512 (16 MFMA K-chunks of 32).
+constexpr int range_width(int E) { return (kLdsElems / E) / 32 * 32 < 512 ? (kLdsElems / E) / 32 * 32 : 512; }
 
 MoeGeom moe_geom(int64_t T, int64_t Hd, int64_t E) {
     MoeGeom g;
     g.ntb = ceil_div(T, TBM);
-    int hr = int(kLdsElems / E) / 32 * 32;
-    if (hr > 512) hr = 512;
-    while (hr > 128 && g.ntb * ceil_div(Hd, hr) < 256) hr = hr / 2 / 32 * 32;
-    g.hr = hr;
-    g.nranges = ceil_div(Hd, hr);
-    g.cnt_bytes = size_t(ceil_div(g.ntb * 4, 256) * 256);
+    g.hr = range_width(int(E));
+    g.nranges = ceil_div(Hd, g.hr);
     g.part_bytes = size_t(g.ntb * g.nranges * TBM * E * 4);
     return g;
 }
@@ -77,17 +80,16 @@ __device__ __forceinline__ void topk_insert(float (&ts)[K], int (&ti)[K], float 
     }
 }
 
-template <int NEB, int K>
-__global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ wg, int64_t T,
-                                                        int64_t Hd, int hr, int64_t nranges, int swz, int k,
-                                                        int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                        float* __restrict__ scores, unsigned* __restrict__ cnt,
-                                                        float* __restrict__ part) {
+// Phase 1: partial scores of 64 tokens over one hidden range.
+template <int NEB>
+__global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wg, int64_t T,
+                                                          int64_t Hd, int hr, int64_t nranges, int swz,
+                                                          float* __restrict__ part) {
     constexpr int E = NEB * 16;
     constexpr int CH = E / 8;         // 16-byte chunks per W row
+    constexpr int NCH = range_width(E) / 32;   // K-chunks of a full range (the last range may be shorter)
     __shared__ __attribute__((aligned(16))) uint16_t wsm[kLdsElems];
-    __shared__ int sm_last;
 
     const int64_t tb = blockIdx.x / nranges;
     const int64_t rg = blockIdx.x - tb * nranges;
@@ -96,49 +98,81 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restri
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
 
-    // Stage W[h0 .. h0 + hlen) (row-major [hd][E]) in LDS; 16-byte chunks swizzled per row.
-    for (int i = tid; i < hlen * CH; i += 256) {
-        const int row = i / CH, ch = i - row * CH;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(wg + (h0 + row) * E + ch * 8);
-        const int pc = ch ^ (((row & 3) << 1) & swz);
-        *reinterpret_cast<u32x4*>(&wsm[row * E + pc * 8]) = val;
+    // Issue every load of the workgroup before waiting on any: the W slice goes to LDS,
+    // the X operands to registers.
+    //
+    // W[h0 .. h0 + hlen) is row-major [hd][E] in LDS with its 16-byte chunks swizzled
+    // per row. When a row has a power-of-two number of chunks, direct global-to-LDS
+    // loads fill it (one wave instruction = 1 KiB = 64 / CH rows; lane i lands in row
+    // i / CH, physical chunk i % CH, so it fetches the logical chunk that maps there).
+    if constexpr ((CH & (CH - 1)) == 0) {
+        constexpr int RPW = 64 / CH;
+        const int nwl = hlen / RPW;
+        for (int wl = wave; wl < nwl; wl += 4) {
+            const int r0 = wl * RPW;
+            const int row = r0 + lane / CH;
+            const int ch = (lane % CH) ^ (((row & 3) << 1) & swz);
+            __builtin_amdgcn_global_load_lds((const void*)(wg + (h0 + row) * E + ch * 8),
+                                             (__attribute__((address_space(3))) void*)(&wsm[r0 * E]), 16, 0, 0);
+        }
+    } else {
+        for (int i0 = 0; i0 < hlen * CH; i0 += 8 * 256) {
+            u32x4 val[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 256 + tid;
+                if (i < hlen * CH) {
+                    const int row = i / CH, ch = i - row * CH;
+                    val[u] = *reinterpret_cast<const u32x4*>(wg + (h0 + row) * E + ch * 8);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 256 + tid;
+                if (i < hlen * CH) {
+                    const int row = i / CH, ch = i - row * CH;
+                    *reinterpret_cast<u32x4*>(&wsm[row * E + ch * 8]) = val[u];   // no swizzle (swz = 0)
+                }
+            }
+        }
     }
 
     // A operand: lane (token l16 of this wave's 16, group g) holds X[token][h0 + 32c + 8g .. +7].
     int64_t tok = tb * TBM + 16 * wave + l16;
     tok = tok < T ? tok : T - 1;
     const uint16_t* xr = x + tok * Hd + h0 + 8 * g;
+    const int nc = hlen / 32;                 // <= NCH
+    u32x4 xa[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int cc = c < nc ? c : nc - 1;   // the tail range re-reads its last chunk (unused)
+        xa[c] = *reinterpret_cast<const u32x4*>(xr + 32 * cc);
+    }
+
     f32x4 acc[NEB];
 #pragma unroll
     for (int b = 0; b < NEB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int nc = hlen / 32;
     const int j = l16;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-        u32x4 xa[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (c0 + u < nc) xa[u] = *reinterpret_cast<const u32x4*>(xr + 32 * (c0 + u));
+    for (int c = 0; c < NCH; ++c) {
+        if (c >= nc) continue;                // uniform: only the last range is shorter
+        // B operand: lane (expert l16 of block b, group g) holds W[32c + 8g + e][16b + l16];
+        // group lane j reads rows 32c + 8g + j/4 (+4), columns 16b + 4(j%4) .. +3.
+        const int r0 = 32 * c + 8 * g + (j >> 2);
+        const int r1 = r0 + 4;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (c0 + u >= nc) break;
-            const int c = c0 + u;
-            // B operand: lane (expert l16 of block b, group g) holds W[32c + 8g + e][16b + l16];
-            // group lane j reads rows 32c + 8g + j/4 (+4), columns 16b + 4(j%4) .. +3.
-            const int r0 = 32 * c + 8 * g + (j >> 2);
-            const int r1 = r0 + 4;
-#pragma unroll
-            for (int b = 0; b < NEB; ++b) {
-                const int col = 16 * b + 4 * (j & 3);
-                const int p0 = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
-                const int p1 = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
-                const bf16x4_t lo = lds_read_tr16(wsm + p0);
-                const bf16x4_t hi = lds_read_tr16(wsm + p1);
-                const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u]),
-                                                                  __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0, 0);
-            }
+        for (int b = 0; b < NEB; ++b) {
+            const int col = 16 * b + 4 * (j & 3);
+            const int p0 = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
+            const int p1 = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
+            const bf16x4_t lo = lds_read_tr16(wsm + p0);
+            const bf16x4_t hi = lds_read_tr16(wsm + p1);
+            const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[c]),
+                                                              __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0, 0);
         }
     }
 
@@ -149,19 +183,18 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restri
 #pragma unroll
         for (int r = 0; r < 4; ++r) pblk[(16 * wave + 4 * g + r) * E + 16 * b + l16] = acc[b][r];
 
-    // Publish the partial block; the last workgroup of this token block reduces.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = atomicAdd(&cnt[tb], 1u);
-        sm_last = old == unsigned(nranges - 1);
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    __threadfence();
+}
 
-    // Reduction: wave w handles tokens 16w .. 16w + 15; four lanes per token, each
-    // owning a contiguous quarter of the experts.
+// Phase 2: one wave per 16 tokens; four lanes per token, each owning a contiguous
+// quarter of the experts.
+template <int NEB, int K>
+__global__ __launch_bounds__(64) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
+                                                        int k, int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                        float* __restrict__ scores) {
+    constexpr int E = NEB * 16;
+    const int lane = threadIdx.x;
+    const int64_t tb = blockIdx.x >> 2;        // token block of 64
+    const int wave = int(blockIdx.x & 3);      // which 16 tokens of it
     constexpr int EQ = E / 4;
     const int tt = lane >> 2, qq = lane & 3;
     const int tl = 16 * wave + tt;
@@ -175,23 +208,41 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restri
         ti[r] = 0x7FFFFFFF;
     }
     if (valid) {
+        // Sum the range partials in range order (deterministic), loading up to RB ranges'
+        // worth of this lane's quarter before adding, so the loads overlap.
+        constexpr int NF4 = EQ / 4;
+        constexpr int RB = NF4 >= 32 ? 1 : 32 / NF4;
         const float* base = part + (tb * nranges * TBM + tl) * E + qq * EQ;
+        float4 s4[NF4];
 #pragma unroll
-        for (int e4 = 0; e4 < EQ; e4 += 4) {
-            float4 s4 = *reinterpret_cast<const float4*>(base + e4);
-            for (int64_t r = 1; r < nranges; ++r) {
-                const float4 p4 = *reinterpret_cast<const float4*>(base + r * TBM * E + e4);
-                s4.x += p4.x;
-                s4.y += p4.y;
-                s4.z += p4.z;
-                s4.w += p4.w;
-            }
-            if (scores) *reinterpret_cast<float4*>(scores + t_out * E + qq * EQ + e4) = s4;
-            const int e0 = qq * EQ + e4;
-            topk_insert<K>(ts, ti, s4.x, e0);
-            topk_insert<K>(ts, ti, s4.y, e0 + 1);
-            topk_insert<K>(ts, ti, s4.z, e0 + 2);
-            topk_insert<K>(ts, ti, s4.w, e0 + 3);
+        for (int f = 0; f < NF4; ++f) s4[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t r0 = 0; r0 < nranges; r0 += RB) {
+            float4 buf[RB][NF4];
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr)
+                if (r0 + rr < nranges)
+#pragma unroll
+                    for (int f = 0; f < NF4; ++f)
+                        buf[rr][f] = *reinterpret_cast<const float4*>(base + (r0 + rr) * TBM * E + 4 * f);
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr)
+                if (r0 + rr < nranges)
+#pragma unroll
+                    for (int f = 0; f < NF4; ++f) {
+                        s4[f].x += buf[rr][f].x;
+                        s4[f].y += buf[rr][f].y;
+                        s4[f].z += buf[rr][f].z;
+                        s4[f].w += buf[rr][f].w;
+                    }
+        }
+#pragma unroll
+        for (int f = 0; f < NF4; ++f) {
+            const int e0 = qq * EQ + 4 * f;
+            if (scores) *reinterpret_cast<float4*>(scores + t_out * E + e0) = s4[f];
+            topk_insert<K>(ts, ti, s4[f].x, e0);
+            topk_insert<K>(ts, ti, s4[f].y, e0 + 1);
+            topk_insert<K>(ts, ti, s4[f].z, e0 + 2);
+            topk_insert<K>(ts, ti, s4[f].w, e0 + 3);
         }
     }
     // Merge the four lanes' lists (lanes differing in bits 0 and 1).
@@ -226,42 +277,42 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restri
             }
         }
     }
-    if (tid == 0) cnt[tb] = 0u;   // every other workgroup of this block has already counted
 }
 
 template <int NEB>
-hipError_t launch_e(int k, dim3 grid, hipStream_t stream, const uint16_t* x, const uint16_t* w, int64_t T, int64_t Hd,
-                    int hr, int64_t nranges, int swz, int32_t* idx, float* wout, float* scores, unsigned* cnt,
-                    float* part) {
+hipError_t launch_e(int k, const MoeGeom& g, int swz, hipStream_t stream, const uint16_t* x, const uint16_t* w,
+                    int64_t T, int64_t Hd, int32_t* idx, float* wout, float* scores, float* part) {
+    const dim3 grid1{unsigned(g.ntb * g.nranges), 1u, 1u};
+    hipLaunchKernelGGL((moe_partial_kernel<NEB>), grid1, dim3(256), 0, stream, x, w, T, Hd, g.hr, g.nranges, swz,
+                       part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid2{unsigned(g.ntb * 4), 1u, 1u};
     // A top-2 fast path; any other k up to 8 keeps an 8-entry list.
     if (k == 2)
-        hipLaunchKernelGGL((moe_route_kernel<NEB, 2>), grid, dim3(256), 0, stream, x, w, T, Hd, hr, nranges, swz, k,
-                           idx, wout, scores, cnt, part);
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(64), 0, stream, part, T, g.nranges, k, idx, wout,
+                           scores);
     else
-        hipLaunchKernelGGL((moe_route_kernel<NEB, 8>), grid, dim3(256), 0, stream, x, w, T, Hd, hr, nranges, swz, k,
-                           idx, wout, scores, cnt, part);
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(64), 0, stream, part, T, g.nranges, k, idx, wout,
+                           scores);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E) {
-    const MoeGeom g = moe_geom(T, Hd, E);
-    return g.cnt_bytes + g.part_bytes;
+    return moe_geom(T, Hd, E).part_bytes;
 }
 
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd, int E, int k,
                             int32_t* idx, float* w, float* scores, void* workspace, hipStream_t stream) {
     const MoeGeom g = moe_geom(T, Hd, E);
-    const int64_t blocks = g.ntb * g.nranges;
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (g.ntb * g.nranges > INT32_MAX || g.ntb * 4 > INT32_MAX) return hipErrorInvalidValue;
     const int CH = E / 8;
     const int swz = (CH >= 8 && (CH & (CH - 1)) == 0) ? 6 : 0;
-    unsigned* cnt = static_cast<unsigned*>(workspace);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.cnt_bytes);
-    const dim3 grid{unsigned(blocks), 1u, 1u};
+    float* part = static_cast<float*>(workspace);
 #define RF_MOE_E(NB) \
-    case NB: return launch_e<NB>(k, grid, stream, x, w_gate, T, Hd, g.hr, g.nranges, swz, idx, w, scores, cnt, part);
+    case NB: return launch_e<NB>(k, g, swz, stream, x, w_gate, T, Hd, idx, w, scores, part);
     switch (E / 16) {
         RF_MOE_E(1) RF_MOE_E(2) RF_MOE_E(3) RF_MOE_E(4) RF_MOE_E(5) RF_MOE_E(6) RF_MOE_E(7) RF_MOE_E(8)
         RF_MOE_E(9) RF_MOE_E(10) RF_MOE_E(11) RF_MOE_E(12) RF_MOE_E(13) RF_MOE_E(14) RF_MOE_E(15) RF_MOE_E(16)

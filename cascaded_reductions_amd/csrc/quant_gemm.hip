@@ -9,9 +9,10 @@
 // section 3.3):
 //  1. quant_rows: one workgroup per row keeps the row in registers, reduces the
 //     absolute maximum (an integer max over the bf16 magnitude bits), forms
-//     sigma = a / 448 and each code from the IEEE fp32 quotient x / sigma with
-//     the hardware round-to-nearest-even E4M3FN conversion (v_cvt_pk_fp8_f32,
-//     which keeps the sign of zero and saturates at 448);
+//     sigma = a / 448 and each code from the IEEE fp32 quotient x / sigma
+//     (reciprocal + one FMA correction, correctly rounded) with the hardware
+//     round-to-nearest-even E4M3FN conversion (v_cvt_pk_fp8_f32, which keeps the
+//     sign of zero and saturates at 448);
 //  2. fp8_gemm: 256 x 256 output tiles, 8 waves, K steps of 128 code bytes
 //     double buffered in LDS (filled by direct global-to-LDS loads, so no
 //     registers are spent on staging). Both operands are K-contiguous, so no
@@ -36,7 +37,6 @@ namespace {
 // ------------------------------------------------------------------ 1. per-row quantisation
 
 constexpr int QT = 256;   // threads per row
-constexpr int QC = 4;     // 16-byte chunks kept in registers per thread (rows up to 8192)
 
 __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -44,6 +44,23 @@ __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
     return uint32_t(v);
 }
 
+// The IEEE fp32 quotient x / sigma from the correctly rounded reciprocal r = 1 / sigma:
+// q0 = x r is within one ulp of x / sigma, the residual x - q0 sigma is exact in one
+// FMA, and q0 + residual * r rounded once is the correctly rounded quotient
+// (Markstein, IBM J. Res. Dev. 34(1), 1990). Overflow cannot occur (|q| <= 448) and an
+// underflowing quotient is far below the smallest E4M3FN subnormal, so its code (+-0)
+// does not depend on the last bits. The correction turns x = -0 into +0, so the sign
+// is restored from x (sigma > 0: the quotient always has the sign of x).
+__device__ __forceinline__ float div_rn(float x, float sigma, float r) {
+    const float q0 = x * r;
+    const float e = fmaf(-q0, sigma, x);
+    return __builtin_copysignf(fmaf(e, r, q0), x);
+}
+
+// One workgroup per row. NCT > 0: the row (at most NCT * QT chunks of 8 values) stays
+// in registers between the absmax pass and the quantisation pass; NCT == 0: the row is
+// read twice.
+template <int NCT>
 __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t K,
                                                         uint8_t* __restrict__ codes, float* __restrict__ xs) {
     __shared__ uint32_t sm_max[QT / 64];
@@ -52,20 +69,26 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
     const uint16_t* xr = x + row * K;
     uint8_t* cr = codes + row * K;
     const int nch = int(K / 8);
-    const bool cached = nch <= QT * QC;
 
-    u32x4 v[QC];
-    uint32_t amax = 0;   // max of the bf16 magnitude bits: ordered like the magnitudes
-    for (int i = 0; i < (nch + QT - 1) / QT; ++i) {
-        const int ch = tid + i * QT;
-        if (ch >= nch) break;
-        const u32x4 t = *reinterpret_cast<const u32x4*>(xr + ch * 8);
-        if (i < QC) v[i] = t;
+    auto absmax8 = [](const u32x4& t, uint32_t m) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            amax = max(amax, t[w] & 0x7FFFu);
-            amax = max(amax, (t[w] >> 16) & 0x7FFFu);
+            m = max(m, t[w] & 0x7FFFu);             // bf16 magnitude bits order like the magnitudes
+            m = max(m, (t[w] >> 16) & 0x7FFFu);
         }
+        return m;
+    };
+    uint32_t amax = 0;
+    u32x4 v[NCT > 0 ? NCT : 1];
+    if constexpr (NCT > 0) {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) {
+            const int ch = tid + i * QT;
+            v[i] = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+            amax = absmax8(v[i], amax);
+        }
+    } else {
+        for (int ch = tid; ch < nch; ch += QT) amax = absmax8(*reinterpret_cast<const u32x4*>(xr + ch * 8), amax);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = max(amax, uint32_t(__shfl_xor(int(amax), m, 64)));
@@ -76,25 +99,32 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
     for (int w = 1; w < QT / 64; ++w) amax = max(amax, sm_max[w]);
 
     const float a = bf16_to_f32(amax);
-    const float sigma = a / 448.0f;      // IEEE fp32 division
+    const float sigma = a / 448.0f;            // IEEE fp32 division
+    const float r = 1.0f / sigma;              // IEEE fp32 division (inf for a zero row; unused then)
     if (tid == 0) xs[row] = sigma;
 
-    for (int i = 0; i < (nch + QT - 1) / QT; ++i) {
-        const int ch = tid + i * QT;
-        if (ch >= nch) break;
-        const u32x4 t = (cached && i < QC) ? v[i] : *reinterpret_cast<const u32x4*>(xr + ch * 8);
-        uint32_t out[2] = {0u, 0u};
+    auto quant8 = [&](const u32x4& t, int ch) {
+        uint32_t out0 = 0u, out1 = 0u;
         if (sigma > 0.f) {
             float q[8];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                q[2 * w] = bf16_lo(t[w]) / sigma;       // IEEE fp32 quotient
-                q[2 * w + 1] = bf16_hi(t[w]) / sigma;
+                q[2 * w] = div_rn(bf16_lo(t[w]), sigma, r);
+                q[2 * w + 1] = div_rn(bf16_hi(t[w]), sigma, r);
             }
-            out[0] = codes4(q[0], q[1], q[2], q[3]);
-            out[1] = codes4(q[4], q[5], q[6], q[7]);
+            out0 = codes4(q[0], q[1], q[2], q[3]);
+            out1 = codes4(q[4], q[5], q[6], q[7]);
         }
-        *reinterpret_cast<uint2*>(cr + ch * 8) = make_uint2(out[0], out[1]);
+        *reinterpret_cast<uint2*>(cr + ch * 8) = make_uint2(out0, out1);
+    };
+    if constexpr (NCT > 0) {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) {
+            const int ch = tid + i * QT;
+            if (ch < nch) quant8(v[i], ch);
+        }
+    } else {
+        for (int ch = tid; ch < nch; ch += QT) quant8(*reinterpret_cast<const u32x4*>(xr + ch * 8), ch);
     }
 }
 
@@ -243,7 +273,15 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, float* x_scale,
                              hipStream_t stream) {
     if (M > INT32_MAX || K / 8 > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(M)), dim3(QT), 0, stream, x, K, codes, x_scale);
+    const int64_t nct = ceil_div(K / 8, QT);
+    const dim3 grid{unsigned(M), 1u, 1u};
+    switch (nct) {
+        case 1: hipLaunchKernelGGL(quant_rows_kernel<1>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
+        case 2: hipLaunchKernelGGL(quant_rows_kernel<2>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
+        case 3: hipLaunchKernelGGL(quant_rows_kernel<3>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
+        case 4: hipLaunchKernelGGL(quant_rows_kernel<4>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
+        default: hipLaunchKernelGGL(quant_rows_kernel<0>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
+    }
     return hipGetLastError();
 }
 

@@ -147,27 +147,24 @@ RF_API size_t rf_moe_route_workspace_size(int64_t T, int64_t Hd, int64_t E);
 /*
  * rf_moe_route -- fused MoE gate: scores = X W_gate -> top-k -> softmax over the k.
  *
- * The cascade of the explainer's section 4.2 in one kernel launch; the full
- * score matrix never reaches memory (unless the optional debug output is
- * requested). Experts are ordered by descending score, equal scores by the
- * lower expert index. The weights are the softmax of the k selected scores:
+ * The cascade of the explainer's section 4.2; the full score matrix never
+ * reaches memory (unless the optional debug output is requested). Experts are
+ * ordered by descending score, equal scores by the lower expert index. The
+ * weights are the softmax of the k selected scores:
  * w_r = exp(s_r - s_1) / sum_r' exp(s_r' - s_1). Scores accumulate in fp32.
  *
- * The hidden axis is split over workgroups (the Multi-Segment strategy of the
- * technical summary, Methodologie 3, applied to the gate GEMM's sum); each
- * workgroup writes a partial score block to `workspace` and the last workgroup
- * of each token block adds the partials in a fixed order (deterministic) and
- * performs the top-k and the softmax.
+ * The hidden axis is split into ranges (the Multi-Segment strategy of the
+ * technical summary, Methodologie 3, applied to the gate GEMM's sum): a first
+ * launch writes one partial score block per (64-token block, hidden range) to
+ * `workspace`; a second adds each token's partials in a fixed order
+ * (deterministic) and performs the top-k and the softmax.
  *
  *   x       [T, Hd] bf16 tokens.   w_gate  [Hd, E] bf16 (expert index contiguous).
  *   idx     [T, k] int32 expert indices.   w  [T, k] fp32 weights.
  *   scores  [T, E] fp32 debug copy of the gate scores, or NULL.
  *   workspace, ws_bytes  device scratch of at least rf_moe_route_workspace_size(T, Hd, E)
- *           bytes (RF_ERR_BUFFER_TOO_SMALL otherwise). It starts with one 32-bit
- *           counter per block of 64 tokens; the counters must be zero before the
- *           workspace is first used (allocate it zero-filled), and every call
- *           leaves them zero again. Calls that share a workspace must not run
- *           concurrently.
+ *           bytes (RF_ERR_BUFFER_TOO_SMALL otherwise); no initial contents are
+ *           required. Calls that share a workspace must not run concurrently.
  *   Supported: T >= 1; Hd >= 32 and Hd % 32 == 0; 16 <= E <= 256 and E % 16 == 0;
  *   1 <= k <= min(8, E).
  */

@@ -117,7 +117,7 @@ def test_moe_validation(lib):
     assert _moe(lib, idx=P4) == INVALID                     # idx aliases w
     assert _moe(lib, sc=P + 16) == INVALID                  # scores inside x
     need = lib.rf_moe_route_workspace_size(2048, 4096, 64)
-    assert need == 256 + 32 * 8 * 64 * 64 * 4              # counters + 8 hidden ranges of partial scores
+    assert need == 32 * 8 * 64 * 64 * 4                    # 32 token blocks x 8 hidden ranges of partial scores
     assert _moe(lib, ws=None) == TOO_SMALL
     assert _moe(lib, nbytes=lib.rf_moe_route_workspace_size(8, 64, 64) - 1) == TOO_SMALL
     assert _moe(lib, ws=P + 64) == INVALID                  # workspace inside x

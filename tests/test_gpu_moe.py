@@ -64,7 +64,7 @@ def test_exact_ties_prefer_lower_index(rf):
 
 
 def test_repeated_calls_reuse_workspace(rf):
-    """The per-block counters are left at zero: back-to-back calls on one workspace agree."""
+    """Back-to-back calls on one (dirty) workspace agree."""
     x, w = moe_inputs(256, 512, 64, 2, seed=31, w_std=0.5)
     a = _check(rf, x, w, 2, check_scores=False)
     b = _check(rf, x, w, 2, check_scores=False)

@@ -119,3 +119,42 @@ def test_every_code_through_the_weight_operand(rf):
     y = _check(rf, x, wq, np.ones(4, np.float32))
     np.testing.assert_array_equal(y[:codes.size, 0], 448.0 * oracle.e4m3fn_decode(codes))
     np.testing.assert_array_equal(y[:codes.size, 1], 448.0 * oracle.e4m3fn_decode(codes[::-1]))
+
+
+def test_midpoints_round_to_even(rf):
+    """Rows with absmax 448 have sigma = 1, so x / sigma = x exactly: inputs at every
+    midpoint between adjacent E4M3FN values (representable in bf16) must round to the
+    even code, and values one bf16 step either side to the nearer one."""
+    codes = np.arange(0, 126, dtype=np.uint8)
+    lo, hi = oracle.e4m3fn_decode(codes), oracle.e4m3fn_decode(codes + 1)
+    mids = (lo + hi) / 2
+    rows = []
+    for sgn in (1.0, -1.0):
+        for delta in (0, -1, 1):
+            mb = f32_to_bf16_bits((sgn * mids).astype(np.float32)).astype(np.int64)
+            mb = (mb + delta * (1 if sgn > 0 else 1)).astype(np.uint16) if delta else mb.astype(np.uint16)
+            row = np.zeros(128, np.float32)
+            row[:mids.size] = bf16_bits_to_f32(mb)
+            row[127] = 448.0
+            rows.append(row)
+    x = f32_to_bf16_bits(np.stack(rows))
+    wq = np.zeros((16, 128), np.uint8)
+    np.fill_diagonal(wq, 0x38)
+    _check(rf, x, wq, np.ones(16, np.float32))     # codes compared bit-exactly with the oracle
+
+
+def test_long_rows_streaming_path(rf):
+    """Rows longer than the 8192 values kept in registers are read twice."""
+    x, wq, ws = quant_inputs(3, 5, 8448, seed=74)
+    _check(rf, x, wq, ws)
+
+
+def test_signed_zero_inputs(rf):
+    """-0.0 inputs keep their sign through the quotient: code 0x80 (IEEE -0 / sigma = -0)."""
+    xf = np.zeros((4, 128), np.float32)
+    xf[:, 0] = [1.0, -3.0, 200.0, -0.5]
+    xf[:, 1::2] = -0.0
+    x = f32_to_bf16_bits(xf)
+    wq = np.zeros((8, 128), np.uint8)
+    np.fill_diagonal(wq, 0x38)
+    _check(rf, x, wq, np.ones(8, np.float32))
