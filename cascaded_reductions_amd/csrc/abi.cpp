@@ -117,6 +117,8 @@ rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const
     RF_REQUIRE(prod({B, H, Sq, D}, &nq) && nq < kMaxElems && prod({B, H, Sk, D}, &nk) &&
                    nk < kMaxElems && prod({B, H, Sq}, &nl),
                RF_ERR_UNSUPPORTED, "tensor too large");
+    RF_REQUIRE(dt == RF_F32 || Sk * D < (int64_t(1) << 30), RF_ERR_UNSUPPORTED,
+               "bf16 path needs Sk * D < 2^30 (got Sk=%lld, D=%lld)", (long long)Sk, (long long)D);
     const uint64_t es = dt == RF_F32 ? 4 : 2;
     RF_REQUIRE(!overlap(o, nq * es, q, nq * es) && !overlap(o, nq * es, k, nk * es) &&
                    !overlap(o, nq * es, v, nk * es) && !overlap(lse, nl * 4, q, nq * es) &&

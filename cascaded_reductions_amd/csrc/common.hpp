@@ -79,6 +79,40 @@ __device__ __forceinline__ float row8_sum(float v) {
     return v;
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i writes LDS bytes [lds_base + 16 i, +16). lds_base must be wave-uniform.
+// Issued through inline assembly so the compiler does not track the LDS write: it would
+// otherwise wait for every such load before any LDS read it cannot prove disjoint,
+// including loads of buffers that are only used later. The caller orders them with
+// an explicit "s_waitcnt vmcnt(N)" and a barrier (vmcnt retires loads in issue order,
+// so loads the compiler does not know of can only make its own waits stricter).
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds_base)));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(base), "v"(gptr)
+        : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit global base (SGPR pair) and a per-lane 32-bit
+// byte offset: the address costs no vector instruction.
+__device__ __forceinline__ void lds_dma16_sb(const void* gbase, uint32_t voff_bytes, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_base), "v"(voff_bytes), "s"(gbase)
+        : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (wave-uniform when the pointer is).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
 // Unpack a dword holding two bf16 values (low half first).
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }

@@ -240,31 +240,61 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
     }
 
     // acc[a][b][r] = C^T[n][m]: n = n0 + wn*128 + a*32 + (r/4)*8 + 4g + r%4, m = m0 + wm*64 + b*32 + l32.
+    // Epilogue: scale, round to bf16 and stage the wave's 64 (m) x 128 (n) block in LDS
+    // (the operand stages are free after the last barrier), then write whole rows with
+    // 16-byte stores so every output line is written once and completely.
+    uint16_t* stg = reinterpret_cast<uint16_t*>(&smem[0][0][0]) + wave * (64 * 128);
+    float wsc[4][4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int64_t n = n0 + wn * 128 + a * 32 + q4 * 8 + 4 * g + e;
+                n = n < N ? n : N - 1;
+                wsc[a][q4][e] = ws[n];
+            }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        const int64_t m = m0 + wm * 64 + b * 32 + l32;
-        if (m >= M) continue;
-        const float sx = xs[m];
-        uint16_t* yr = y + m * N;
+        int64_t m = m0 + wm * 64 + b * 32 + l32;
+        const float sx = xs[m < M ? m : M - 1];
+        const int ml = b * 32 + l32;           // row of the staging block
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int64_t n = n0 + wn * 128 + a * 32 + q4 * 8 + 4 * g;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t nn = n + e < N ? n + e : N - 1;
-                    v[e] = (acc[a][b][4 * q4 + e] * sx) * ws[nn];
-                }
-                if (n + 3 < N) {
-                    *reinterpret_cast<uint2*>(yr + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) yr[n + e] = uint16_t(f32_to_bf16_rne(v[e]));
-                }
+                const int nl = a * 32 + q4 * 8 + 4 * g;   // column of the staging block (multiple of 4)
+                const f32x16& c = acc[a][b];
+                const uint2 w2 = make_uint2(
+                    pack_bf16x2((c[4 * q4 + 0] * sx) * wsc[a][q4][0], (c[4 * q4 + 1] * sx) * wsc[a][q4][1]),
+                    pack_bf16x2((c[4 * q4 + 2] * sx) * wsc[a][q4][2], (c[4 * q4 + 3] * sx) * wsc[a][q4][3]));
+                // 16-byte chunks of a staging row are rotated by the row index to spread banks.
+                const int chunk = ((nl >> 3) + ml) & 15;
+                *reinterpret_cast<uint2*>(stg + ml * 128 + chunk * 8 + (nl & 7)) = w2;
             }
+    }
+    __syncthreads();
+    // 64 rows x 16 chunks of 16 bytes: each instruction writes 4 whole rows.
+    const int64_t nbase = n0 + wn * 128;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int ml = it * 4 + (lane >> 4);
+        const int ch = lane & 15;
+        const int64_t m = m0 + wm * 64 + ml;
+        const int64_t n = nbase + ch * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + ml * 128 + (((ch + ml) & 15) * 8));
+        if (m < M) {
+            uint16_t* dst = y + m * N + n;
+            if (n + 7 < N && ((N & 7) == 0)) {
+                *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+                const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = hv[e];
+            }
+        }
     }
 }
 

@@ -92,7 +92,8 @@ RF_API const char* rf_last_error(void);
  *   lse    [B, H, Sq] fp32 natural-log logsumexp of the scaled scores,
  *          m + ln(s); may be NULL.
  *   scale  the softmax scale applied to Q K^T before the maximum.
- *   Supported: B, H, Sq, Sk >= 1; D in {64, 128}; B*H*Sq*D and B*H*Sk*D below 2^40.
+ *   Supported: B, H, Sq, Sk >= 1; D in {64, 128}; B*H*Sq*D and B*H*Sk*D below 2^40;
+ *   for RF_BF16 also Sk*D below 2^30.
  *   Accumulation is fp32. bf16 outputs are rounded to nearest even.
  */
 RF_API rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const void* v,
