@@ -63,7 +63,7 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
 }
 
-template <int D, int STAGES>
+template <int D, int STAGES, bool EXACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1)))
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
@@ -147,7 +147,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         t = t < nt ? t : nt - 1;
         const uint16_t* gbase = ld_src + int64_t(t) * KT * D;   // scalar
         const uint32_t lbase = ld_lds0 + uint32_t(stage * SLOT * 2);
-        if (t * KT + KT <= sk) {
+        if (EXACT || t * KT + KT <= sk) {
 #pragma unroll
             for (int l = 0; l < WL; ++l) lds_dma16_sb(gbase, ld_off[l], lbase + l * 1024);
         } else {                              // the last tile runs past the key axis: clamp rows
@@ -271,6 +271,110 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         }
     };
 
+    if constexpr (EXACT) {
+        // ---- key axis a multiple of 2 * KT: every tile full, nsteps per key half -----------
+        // The loop of the general path below without its tail cases. Ring slots repeat
+        // every 3 steps and the two score buffers every 2, so the loop is unrolled 6 times
+        // and neither buffer is ever copied. The reference maximum starts at the first
+        // tile's maximum; afterwards a tile's row maximum is only formed when needed: a
+        // lane whose probabilities (against the current reference) sum to at most 2^8 has
+        // every probability at most 2^8, which is all the lazy reference requires, so only
+        // a larger or non-finite sum sends the wave through the exact path (row maximum,
+        // move of the reference if the maximum is above it, probabilities again).
+        const bool k_loader = ld_kind == 0;
+        issue(0, 0);
+        issue(1, 1);
+        if (k_loader) issue(2, 2);
+        if (k_loader) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL) : "memory");   // K(0) is in
+        __syncthreads();
+        f32x16 sa = scores(0), sb;
+        m_ref = rowmax2(sa);
+        auto probs_sum = [&](const f32x16& sc, uint32_t (&pk)[8]) {
+            float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float p0 = exp2_fast(fmaf(sc[r], sl2, -m_ref));
+                const float p1 = exp2_fast(fmaf(sc[r + 1], sl2, -m_ref));
+                const float p2 = exp2_fast(fmaf(sc[r + 2], sl2, -m_ref));
+                const float p3 = exp2_fast(fmaf(sc[r + 3], sl2, -m_ref));
+                pk[r >> 1] = pack_bf16(p0, p1);
+                pk[(r >> 1) + 1] = pack_bf16(p2, p3);
+                t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), ones, t0, false);
+                t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[(r >> 1) + 1]), ones, t1, false);
+            }
+            return t0 + t1;
+        };
+        auto settle = [&](const f32x16& sc, uint32_t (&pk)[8], float t) {
+            if (__any(!(t <= 256.f))) {
+                const float mx2 = rowmax2(sc);
+                if (mx2 > m_ref) {
+                    const float alpha = exp2_fast(m_ref - mx2);
+                    s_part *= alpha;
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) acc_o[b] *= alpha;
+                    m_ref = mx2;
+                }
+                t = probs_sum(sc, pk);
+            }
+            s_part += t;
+        };
+        auto step = [&](int j, auto ks1_tag, auto vs0_tag, const f32x16& s_cur, f32x16& s_next) {
+            constexpr int KS1 = decltype(ks1_tag)::value;
+            constexpr int VS0 = decltype(vs0_tag)::value;
+            constexpr int VFREE = (VS0 + STAGES - 1) % STAGES;
+            u32x4 kf[NC];
+            uint32_t pk[8];
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // K(j + 1) / V(j) are in
+            __syncthreads();
+            if (k_loader) issue(j + 3, VS0);
+            else issue(j + 2, VFREE);
+            load_k(KS1, kf);
+            s_next = mfma_s(kf);
+            float t = probs_sum(s_cur, pk);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);   // then VALU work
+            }
+            settle(s_cur, pk, t);
+            pv(VS0, pk);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        const int nst = nsteps - 1;           // steps with a successor
+        int j = 0;
+        for (; j + 6 <= nst; j += 6) {
+            step(j, I1{}, I0{}, sa, sb);
+            step(j + 1, I2{}, I1{}, sb, sa);
+            step(j + 2, I0{}, I2{}, sa, sb);
+            step(j + 3, I1{}, I0{}, sb, sa);
+            step(j + 4, I2{}, I1{}, sa, sb);
+            step(j + 5, I0{}, I2{}, sb, sa);
+        }
+        if (j < nst) {
+            step(j, I1{}, I0{}, sa, sb);
+            if (j + 1 < nst) {
+                step(j + 1, I2{}, I1{}, sb, sa);
+                if (j + 2 < nst) {
+                    step(j + 2, I0{}, I2{}, sa, sb);
+                    if (j + 3 < nst) {
+                        step(j + 3, I1{}, I0{}, sb, sa);
+                        if (j + 4 < nst) step(j + 4, I2{}, I1{}, sa, sb);
+                    }
+                }
+            }
+        }
+        {   // the last step: its scores sit in sa (nst even) or sb, its V tile in slot nst % 3
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // V(nst) is in
+            __syncthreads();
+            const f32x16 sl = (nst & 1) ? sb : sa;
+            uint32_t pk[8];
+            const float t = probs_sum(sl, pk);
+            settle(sl, pk, t);
+            pv(nst % 3, pk);
+        }
+    } else {
     // ---- the pipelined loop ------------------------------------------------------------
     // Iteration j works on step j (scores s_cur and row maximum mx_cur already known) and
     // prepares step j + 1:
@@ -358,6 +462,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         if (j + 1 < nsteps) iteration(j + 1, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
         if (j + 2 < nsteps) iteration(j + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
     }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // retire the trailing (unused) loads
 
     // Merge the two key halves of each query block: half 1 publishes (ref, s, o~) in
@@ -405,7 +510,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
     }
 }
 
-template <int D, int STAGES>
+template <int D, int STAGES, bool EXACT>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int64_t BH,
                     int64_t Sq, int64_t Sk, float scale, hipStream_t stream) {
     const int64_t nqb = ceil_div(Sq, 64);
@@ -413,8 +518,8 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uin
     if (blocks > INT32_MAX || nqb > INT32_MAX) return hipErrorInvalidValue;
     const float sl2 = (scale < 0.f ? -scale : scale) * kLog2e;
     const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, STAGES>), dim3(unsigned(blocks)), dim3(256), 0, stream, q, k, v, o,
-                       lse, Sq, Sk, int(nqb), sl2, qsign);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, STAGES, EXACT>), dim3(unsigned(blocks)), dim3(256), 0, stream, q, k,
+                       v, o, lse, Sq, Sk, int(nqb), sl2, qsign);
     return hipGetLastError();
 }
 
@@ -422,8 +527,12 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uin
 
 hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                 int64_t BH, int64_t Sq, int64_t Sk, int D, float scale, hipStream_t stream) {
-    if (D == 64) return launch_t<64, 3>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
-    return launch_t<128, 3>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    const bool exact = Sk % (2 * KT) == 0;
+    if (D == 64)
+        return exact ? launch_t<64, 3, true>(q, k, v, o, lse, BH, Sq, Sk, scale, stream)
+                     : launch_t<64, 3, false>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
+    return exact ? launch_t<128, 3, true>(q, k, v, o, lse, BH, Sq, Sk, scale, stream)
+                 : launch_t<128, 3, false>(q, k, v, o, lse, BH, Sq, Sk, scale, stream);
 }
 
 }  // namespace rf

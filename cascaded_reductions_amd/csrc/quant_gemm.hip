@@ -135,6 +135,7 @@ constexpr int BK = 128;        // bytes of K per step
 constexpr int GW = 8;          // waves
 constexpr int GT = GW * 64;    // threads
 constexpr int TILE_BYTES = BT * BK;                     // 32 KiB per operand per stage
+constexpr int GM = 8;          // tile columns per group in the tile order (see tile_of)
 
 // Eight E4M3FN codes (two dwords) -> eight bf16 values. Every E4M3FN value is exactly
 // representable in bf16, so the conversion (v_cvt_scalef32_pk_bf16_fp8, scale 1) is exact.
@@ -152,17 +153,30 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // LDS row of 128 bytes = 8 chunks of 16 bytes, chunk index XOR-swizzled by row.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so workgroup b runs
+// on XCD b % 8; renumbering makes each XCD own a contiguous range of logical tiles. The
+// logical order walks groups of GM tile columns (M) with the tile rows (N) inside, so an
+// XCD's range of 32 tiles at 16 x 16 tiles is a 4 (N) x 8 (M) block: it reads 4 W panels
+// and 8 X panels into its L2 instead of 2 and 16.
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t total, int64_t tiles_m, int64_t tiles_n, int64_t& tn,
+                                        int64_t& tm) {
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int64_t group = bid / (GM * tiles_n);
+    const int64_t first = group * GM;
+    const int64_t width = tiles_m - first < GM ? tiles_m - first : GM;
+    const int64_t in = bid - group * GM * tiles_n;
+    tn = in / width;
+    tm = first + (in - tn * width);
+}
+
 __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq,
                                                       const float* __restrict__ xs, const float* __restrict__ ws,
-                                                      int64_t M, int64_t N, int64_t K, int tiles_m,
+                                                      int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
                                                       uint16_t* __restrict__ y) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILE_BYTES];   // [stage][W, X]
 
-    // Tile order: XCD-major so that the tiles one XCD runs share operand rows in its L2.
-    int64_t bid = blockIdx.x;
-    const int64_t total = int64_t(gridDim.x);
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int64_t tn = bid / tiles_m, tm = bid - tn * tiles_m;
+    int64_t tn, tm;
+    tile_of(blockIdx.x, int64_t(gridDim.x), tiles_m, tiles_n, tn, tm);
     const int64_t n0 = tn * BT, m0 = tm * BT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -321,7 +335,7 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* b, const float* sa, 
     const int64_t blocks = tm * tn;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fp8_gemm_kernel, dim3(unsigned(blocks)), dim3(GT), 0, stream, a, b, sa, sb, M, N, K, int(tm),
-                       y);
+                       int(tn), y);
     return hipGetLastError();
 }
 

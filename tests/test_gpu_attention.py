@@ -110,3 +110,46 @@ def test_bf16_deterministic(rf):
     o1, l1 = _run(rf, inp)
     o2, l2 = _run(rf, inp)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("Sk,D,scale", [
+    (128, 64, 0.125),      # two steps per key half
+    (192, 64, 0.125),      # three steps: remainder of the unrolled loop
+    (384, 128, 0.0883883), # six steps: the longest remainder, D = 128
+    (448, 64, 0.125),      # seven steps: one whole unrolled round, no remainder
+    (832, 64, 0.125),      # thirteen steps: two rounds
+    (1024, 64, 3.0),       # large scores: the exact path moves the reference
+    (128, 64, 0.0),        # scale 0
+    (256, 128, -0.25),     # negative scale, D = 128
+])
+def test_bf16_whole_tiles(rf, Sk, D, scale):
+    """Key lengths that are multiples of 64 take the loop without tail handling."""
+    inp = attn_inputs(2, 2, 70, Sk, D, "bf16", seed=900 + Sk + D, scale=scale)
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+def test_bf16_stepped_scores(rf):
+    """Tiles of 32 keys whose scores are shifted by a per-tile offset (in units of ln 2 after
+    scaling): a tile a few units above the reference makes its probability sum exceed 2^8
+    without any probability doing so, one far above forces a rescale, and tiles far below
+    underflow."""
+    from synth import f32_to_bf16_bits
+    Sk, D = 512, 64
+    inp = attn_inputs(1, 2, 64, Sk, D, "bf16", seed=23, scale=0.125)
+    qf = bf16_bits_to_f32(inp.q)
+    kf = bf16_bits_to_f32(inp.k).copy()
+    offs = np.array([0, 5, 5, 7, -30, 12, 2, 14, 14, 9, 20, 0, 6, 6, 30, 1], np.float32)   # per 32-key tile
+    # Shift every key of tile t so that each query's score moves by about offs[t] * ln 2:
+    # add c * mean(q) direction, scaled so that scale * q . dk = offs[t] * ln(2) on average.
+    qm = qf.mean(axis=2, keepdims=True)                      # [B,H,1,D]
+    nrm = (qm ** 2).sum(axis=3, keepdims=True)
+    for t, off in enumerate(offs):
+        kf[:, :, 32 * t:32 * (t + 1), :] += qm * (off * np.log(2) / inp.scale / nrm)
+    inp.k = f32_to_bf16_bits(kf.astype(np.float32))
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
