@@ -50,6 +50,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int KT = 32;              // keys per tile (per key half)
 constexpr float kRescaleSlack = 8.f;
@@ -254,7 +255,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         }
     };
     // O^T += V^T P^T over two 16-key chunks.
-    auto pv = [&](int stage, const uint32_t (&pk)[8]) {
+    auto pv = [&](int stage, const auto& pk) {
         const uint16_t* vs = vring + stage * SLOT + kh * TILE;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
@@ -273,23 +274,35 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
 
     if constexpr (EXACT) {
         // ---- key axis a multiple of 2 * KT: every tile full, nsteps per key half -----------
-        // The loop of the general path below without its tail cases. Ring slots repeat
-        // every 3 steps and the two score buffers every 2, so the loop is unrolled 6 times
-        // and neither buffer is ever copied. The reference maximum starts at the first
-        // tile's maximum; afterwards a tile's row maximum is only formed when needed: a
-        // lane whose probabilities (against the current reference) sum to at most 2^8 has
-        // every probability at most 2^8, which is all the lazy reference requires, so only
-        // a larger or non-finite sum sends the wave through the exact path (row maximum,
-        // move of the reference if the maximum is above it, probabilities again).
+        // Step j (of a key half) issues the score MFMAs of tile j + 1 and the PV MFMAs of
+        // tile j - 1 while the vector ALUs form tile j's probabilities, so all eight MFMAs
+        // of a step overlap the softmax work of the same wave. Ring protocol (3 K slots,
+        // 3 V slots): at the top of step j, K(j + 1) and V(j - 1) have landed; the K
+        // loaders then refill K(j)'s slot with K(j + 3) and the V loaders V(j - 2)'s slot
+        // with V(j + 1) (both read for the last time in step j - 1), so every tile is issued
+        // two steps before its first use. Ring slots repeat every 3 steps and the score and
+        // probability buffers every 2, so the loop is unrolled 6 times and no buffer is
+        // ever copied.
+        //
+        // The reference maximum starts at the first tile's maximum; afterwards a tile's row
+        // maximum is only formed when needed: a lane whose probabilities (against the
+        // current reference) sum to at most 2^8 has every probability at most 2^8, which is
+        // all the lazy reference requires, so only a larger or non-finite sum sends the
+        // wave through the exact path (row maximum, move of the reference if the maximum is
+        // above it, probabilities again).
         const bool k_loader = ld_kind == 0;
-        issue(0, 0);
-        issue(1, 1);
-        if (k_loader) issue(2, 2);
-        if (k_loader) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL) : "memory");   // K(0) is in
+        if (k_loader) {
+            issue(0, 0);
+            issue(1, 1);
+            issue(2, 2);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL) : "memory");   // K(0) is in
+        } else {
+            issue(0, 0);
+        }
         __syncthreads();
         f32x16 sa = scores(0), sb;
         m_ref = rowmax2(sa);
-        auto probs_sum = [&](const f32x16& sc, uint32_t (&pk)[8]) {
+        auto probs_sum = [&](const f32x16& sc, u32x8& pk) {
             float t0 = 0.f, t1 = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
@@ -297,14 +310,16 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                 const float p1 = exp2_fast(fmaf(sc[r + 1], sl2, -m_ref));
                 const float p2 = exp2_fast(fmaf(sc[r + 2], sl2, -m_ref));
                 const float p3 = exp2_fast(fmaf(sc[r + 3], sl2, -m_ref));
-                pk[r >> 1] = pack_bf16(p0, p1);
-                pk[(r >> 1) + 1] = pack_bf16(p2, p3);
-                t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), ones, t0, false);
-                t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[(r >> 1) + 1]), ones, t1, false);
+                // (Packed words go through scalars: a bit cast of a vector element reads element 0.)
+                const uint32_t w0 = pack_bf16(p0, p1), w1 = pack_bf16(p2, p3);
+                pk[r >> 1] = w0;
+                pk[(r >> 1) + 1] = w1;
+                t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), ones, t0, false);
+                t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), ones, t1, false);
             }
             return t0 + t1;
         };
-        auto settle = [&](const f32x16& sc, uint32_t (&pk)[8], float t) {
+        auto settle = [&](const f32x16& sc, u32x8& pk, float t) {
             if (__any(!(t <= 256.f))) {
                 const float mx2 = rowmax2(sc);
                 if (mx2 > m_ref) {
@@ -318,61 +333,84 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
             }
             s_part += t;
         };
-        auto step = [&](int j, auto ks1_tag, auto vs0_tag, const f32x16& s_cur, f32x16& s_next) {
-            constexpr int KS1 = decltype(ks1_tag)::value;
-            constexpr int VS0 = decltype(vs0_tag)::value;
-            constexpr int VFREE = (VS0 + STAGES - 1) % STAGES;
+        // One step with a successor tile. J = j mod 3 (compile time).
+        auto step = [&](int j, auto j_tag, auto first_tag, const f32x16& s_cur, f32x16& s_next,
+                        const u32x8& pk_prev, u32x8& pk_cur) {
+            constexpr int J = decltype(j_tag)::value % 3;
+            constexpr bool FIRST = decltype(first_tag)::value;
+            constexpr int KS1 = (J + 1) % 3;     // K(j + 1)
+            constexpr int VP = (J + 2) % 3;      // V(j - 1)
             u32x4 kf[NC];
-            uint32_t pk[8];
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // K(j + 1) / V(j) are in
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // K(j + 1) / V(j - 1) are in
             __syncthreads();
-            if (k_loader) issue(j + 3, VS0);
-            else issue(j + 2, VFREE);
+            if (k_loader) issue(j + 3, J);       // into K(j)'s slot
+            else issue(j + 1, KS1);              // into V(j - 2)'s slot
             load_k(KS1, kf);
             s_next = mfma_s(kf);
-            float t = probs_sum(s_cur, pk);
+            if constexpr (!FIRST) pv(VP, pk_prev);
+            const float t = probs_sum(s_cur, pk_cur);
+            if constexpr (FIRST) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);   // then VALU work
+                for (int c = 0; c < NC; ++c) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);   // then VALU work
+                }
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x100, NC + 4 * DB, 0);   // K and V reads
+#pragma unroll
+                for (int c = 0; c < NC + 2 * DB; ++c) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+                }
             }
-            settle(s_cur, pk, t);
-            pv(VS0, pk);
+            settle(s_cur, pk_cur, t);
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
-        const int nst = nsteps - 1;           // steps with a successor
-        int j = 0;
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        using F = std::false_type;
+        u32x8 pka, pkb;                          // probabilities of even / odd tiles
+        const int nst = nsteps - 1;              // steps with a successor
+        if (nst > 0) step(0, I0{}, std::true_type{}, sa, sb, pkb, pka);
+        int j = 1;
         for (; j + 6 <= nst; j += 6) {
-            step(j, I1{}, I0{}, sa, sb);
-            step(j + 1, I2{}, I1{}, sb, sa);
-            step(j + 2, I0{}, I2{}, sa, sb);
-            step(j + 3, I1{}, I0{}, sb, sa);
-            step(j + 4, I2{}, I1{}, sa, sb);
-            step(j + 5, I0{}, I2{}, sb, sa);
+            step(j, I1{}, F{}, sb, sa, pka, pkb);
+            step(j + 1, I2{}, F{}, sa, sb, pkb, pka);
+            step(j + 2, I3{}, F{}, sb, sa, pka, pkb);
+            step(j + 3, I4{}, F{}, sa, sb, pkb, pka);
+            step(j + 4, I5{}, F{}, sb, sa, pka, pkb);
+            step(j + 5, I0{}, F{}, sa, sb, pkb, pka);
         }
         if (j < nst) {
-            step(j, I1{}, I0{}, sa, sb);
+            step(j, I1{}, F{}, sb, sa, pka, pkb);
             if (j + 1 < nst) {
-                step(j + 1, I2{}, I1{}, sb, sa);
+                step(j + 1, I2{}, F{}, sa, sb, pkb, pka);
                 if (j + 2 < nst) {
-                    step(j + 2, I0{}, I2{}, sa, sb);
+                    step(j + 2, I3{}, F{}, sb, sa, pka, pkb);
                     if (j + 3 < nst) {
-                        step(j + 3, I1{}, I0{}, sb, sa);
-                        if (j + 4 < nst) step(j + 4, I2{}, I1{}, sa, sb);
+                        step(j + 3, I4{}, F{}, sa, sb, pkb, pka);
+                        if (j + 4 < nst) step(j + 4, I5{}, F{}, sb, sa, pka, pkb);
                     }
                 }
             }
         }
-        {   // the last step: its scores sit in sa (nst even) or sb, its V tile in slot nst % 3
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // V(nst) is in
+        {   // The last tile: PV of the one before, its own probabilities, then its PV once
+            // V(nst) has landed. Its scores sit in sa (nst even) or sb.
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // V(nst - 1) is in
             __syncthreads();
-            const f32x16 sl = (nst & 1) ? sb : sa;
-            uint32_t pk[8];
-            const float t = probs_sum(sl, pk);
-            settle(sl, pk, t);
-            pv(nst % 3, pk);
+            const bool odd = nst & 1;
+            const f32x16 sl = odd ? sb : sa;
+            const u32x8 pp = odd ? pka : pkb;
+            u32x8 pl;
+            if (nst > 0) pv((nst + 2) % 3, pp);
+            const float t = probs_sum(sl, pl);
+            settle(sl, pl, t);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // V(nst) is in
+            __syncthreads();
+            pv(nst % 3, pl);
         }
     } else {
     // ---- the pipelined loop ------------------------------------------------------------
