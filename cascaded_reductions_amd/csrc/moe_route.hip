@@ -17,13 +17,15 @@
 //    partial score block to the workspace;
 //  * a second launch adds each token's range partials in range order -- a fixed
 //    order, so results are deterministic -- and runs the top-k and the softmax
-//    in registers: four lanes per token each keep a sorted top-k list over a
-//    quarter of the experts, merged with two cross-lane steps. (Publishing the
+//    in registers: sixteen lanes per token each keep a sorted top-k list over a
+//    sixteenth of the experts, merged with four cross-lane steps. (Publishing the
 //    partials inside one launch would need an agent-scope release per
 //    workgroup, which on gfx950 writes back the whole L2 of the XCD; the
 //    kernel boundary orders the two phases instead -- the explainer's
 //    multi-kernel level, section 3.3.)
 // Experts are ranked by (score descending, index ascending).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -112,8 +114,7 @@ __global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __rest
             const int r0 = wl * RPW;
             const int row = r0 + lane / CH;
             const int ch = (lane % CH) ^ (((row & 3) << 1) & swz);
-            __builtin_amdgcn_global_load_lds((const void*)(wg + (h0 + row) * E + ch * 8),
-                                             (__attribute__((address_space(3))) void*)(&wsm[r0 * E]), 16, 0, 0);
+            lds_dma16(wg + (h0 + row) * E + ch * 8, &wsm[r0 * E]);
         }
     } else {
         for (int i0 = 0; i0 < hlen * CH; i0 += 8 * 256) {
@@ -152,29 +153,42 @@ __global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __rest
     f32x4 acc[NEB];
 #pragma unroll
     for (int b = 0; b < NEB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Only the W slice must be complete before the barrier: the X loads were issued after
+    // it, so waiting until NCH loads remain leaves exactly the X chunks in flight. Chunk c
+    // of X is then waited for just before its MFMAs (the compiler counts those loads), so
+    // the matrix work on the first chunks overlaps the arrival of the later ones. (The W
+    // loads are issued through inline assembly, which keeps the compiler from waiting for
+    // every load before the first LDS read.)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
     __syncthreads();
 
     const int j = l16;
+    // Full ranges take a loop without a chunk test (so no load is sunk below the
+    // barrier); only the last, shorter range skips the chunks past its end.
+    auto mfma_chunks = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        if (c >= nc) continue;                // uniform: only the last range is shorter
-        // B operand: lane (expert l16 of block b, group g) holds W[32c + 8g + e][16b + l16];
-        // group lane j reads rows 32c + 8g + j/4 (+4), columns 16b + 4(j%4) .. +3.
-        const int r0 = 32 * c + 8 * g + (j >> 2);
-        const int r1 = r0 + 4;
+        for (int c = 0; c < NCH; ++c) {
+            if (!FULL && c >= nc) continue;
+            // B operand: lane (expert l16 of block b, group g) holds W[32c + 8g + e][16b + l16];
+            // group lane j reads rows 32c + 8g + j/4 (+4), columns 16b + 4(j%4) .. +3.
+            const int r0 = 32 * c + 8 * g + (j >> 2);
+            const int r1 = r0 + 4;
 #pragma unroll
-        for (int b = 0; b < NEB; ++b) {
-            const int col = 16 * b + 4 * (j & 3);
-            const int p0 = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
-            const int p1 = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
-            const bf16x4_t lo = lds_read_tr16(wsm + p0);
-            const bf16x4_t hi = lds_read_tr16(wsm + p1);
-            const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[c]),
-                                                              __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0, 0);
+            for (int b = 0; b < NEB; ++b) {
+                const int col = 16 * b + 4 * (j & 3);
+                const int p0 = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
+                const int p1 = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
+                const bf16x4_t lo = lds_read_tr16(wsm + p0);
+                const bf16x4_t hi = lds_read_tr16(wsm + p1);
+                const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[c]),
+                                                                  __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0, 0);
+            }
         }
-    }
+    };
+    if (nc == NCH) mfma_chunks(std::true_type{});
+    else mfma_chunks(std::false_type{});
 
     // acc[b][r] = partial score of token (16*wave + 4g + r) for expert 16b + l16.
     float* pblk = part + ((tb * nranges + rg) * TBM) * E;
@@ -185,20 +199,16 @@ __global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __rest
 
 }
 
-// Phase 2: one wave per 16 tokens; four lanes per token, each owning a contiguous
-// quarter of the experts.
+// Phase 2: sixteen lanes per token (4 tokens per wave, 16 per workgroup); lane q of a
+// token owns experts [q * NEB, q * NEB + NEB).
 template <int NEB, int K>
-__global__ __launch_bounds__(64) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
-                                                        int k, int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                        float* __restrict__ scores) {
+__global__ __launch_bounds__(256) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
+                                                         int k, int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                         float* __restrict__ scores) {
     constexpr int E = NEB * 16;
-    const int lane = threadIdx.x;
-    const int64_t tb = blockIdx.x >> 2;        // token block of 64
-    const int wave = int(blockIdx.x & 3);      // which 16 tokens of it
-    constexpr int EQ = E / 4;
-    const int tt = lane >> 2, qq = lane & 3;
-    const int tl = 16 * wave + tt;
-    const int64_t t_out = tb * TBM + tl;
+    const int tid = threadIdx.x;
+    const int q = tid & 15;
+    const int64_t t_out = int64_t(blockIdx.x) * 16 + (tid >> 4);
     const bool valid = t_out < T;
     float ts[K];
     int ti[K];
@@ -208,46 +218,37 @@ __global__ __launch_bounds__(64) void moe_reduce_kernel(const float* __restrict_
         ti[r] = 0x7FFFFFFF;
     }
     if (valid) {
-        // Sum the range partials in range order (deterministic), loading up to RB ranges'
-        // worth of this lane's quarter before adding, so the loads overlap.
-        constexpr int NF4 = EQ / 4;
-        constexpr int RB = NF4 >= 32 ? 1 : 32 / NF4;
-        const float* base = part + (tb * nranges * TBM + tl) * E + qq * EQ;
-        float4 s4[NF4];
+        // Sum the range partials in range order (deterministic), loading RB ranges' worth
+        // of this lane's experts before adding, so the loads overlap.
+        const int64_t tb = t_out / TBM;
+        const int64_t tl = t_out - tb * TBM;
+        const float* base = part + (tb * nranges * TBM + tl) * E + q * NEB;
+        constexpr int RB = NEB >= 8 ? 4 : 8;
+        float sum[NEB];
 #pragma unroll
-        for (int f = 0; f < NF4; ++f) s4[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < NEB; ++e) sum[e] = 0.f;
         for (int64_t r0 = 0; r0 < nranges; r0 += RB) {
-            float4 buf[RB][NF4];
+            float buf[RB][NEB];
 #pragma unroll
             for (int rr = 0; rr < RB; ++rr)
                 if (r0 + rr < nranges)
 #pragma unroll
-                    for (int f = 0; f < NF4; ++f)
-                        buf[rr][f] = *reinterpret_cast<const float4*>(base + (r0 + rr) * TBM * E + 4 * f);
+                    for (int e = 0; e < NEB; ++e) buf[rr][e] = base[(r0 + rr) * TBM * E + e];
 #pragma unroll
             for (int rr = 0; rr < RB; ++rr)
                 if (r0 + rr < nranges)
 #pragma unroll
-                    for (int f = 0; f < NF4; ++f) {
-                        s4[f].x += buf[rr][f].x;
-                        s4[f].y += buf[rr][f].y;
-                        s4[f].z += buf[rr][f].z;
-                        s4[f].w += buf[rr][f].w;
-                    }
+                    for (int e = 0; e < NEB; ++e) sum[e] += buf[rr][e];
         }
 #pragma unroll
-        for (int f = 0; f < NF4; ++f) {
-            const int e0 = qq * EQ + 4 * f;
-            if (scores) *reinterpret_cast<float4*>(scores + t_out * E + e0) = s4[f];
-            topk_insert<K>(ts, ti, s4[f].x, e0);
-            topk_insert<K>(ts, ti, s4[f].y, e0 + 1);
-            topk_insert<K>(ts, ti, s4[f].z, e0 + 2);
-            topk_insert<K>(ts, ti, s4[f].w, e0 + 3);
+        for (int e = 0; e < NEB; ++e) {
+            if (scores) scores[t_out * E + q * NEB + e] = sum[e];
+            topk_insert<K>(ts, ti, sum[e], q * NEB + e);
         }
     }
-    // Merge the four lanes' lists (lanes differing in bits 0 and 1).
+    // Merge the sixteen lanes' lists of a token (lanes differing in bits 0-3).
 #pragma unroll
-    for (int mask = 1; mask <= 2; mask <<= 1) {
+    for (int mask = 1; mask <= 8; mask <<= 1) {
         float os[K];
         int oi[K];
 #pragma unroll
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(64) void moe_reduce_kernel(const float* __restrict_
     }
     // The list holds the K best; the first k (k <= K) are the output, and the
     // softmax runs over exactly those k scores.
-    if (valid && qq == 0) {
+    if (valid && q == 0) {
         float den = 0.f;
         float ex[K];
 #pragma unroll
@@ -287,13 +288,13 @@ hipError_t launch_e(int k, const MoeGeom& g, int swz, hipStream_t stream, const 
                        part);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid2{unsigned(g.ntb * 4), 1u, 1u};
+    const dim3 grid2{unsigned(ceil_div(T, int64_t(16))), 1u, 1u};
     // A top-2 fast path; any other k up to 8 keeps an 8-entry list.
     if (k == 2)
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(64), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(256), 0, stream, part, T, g.nranges, k, idx, wout,
                            scores);
     else
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(64), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(256), 0, stream, part, T, g.nranges, k, idx, wout,
                            scores);
     return hipGetLastError();
 }
@@ -307,7 +308,7 @@ size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E) {
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd, int E, int k,
                             int32_t* idx, float* w, float* scores, void* workspace, hipStream_t stream) {
     const MoeGeom g = moe_geom(T, Hd, E);
-    if (g.ntb * g.nranges > INT32_MAX || g.ntb * 4 > INT32_MAX) return hipErrorInvalidValue;
+    if (g.ntb * g.nranges > INT32_MAX || ceil_div(T, int64_t(16)) > INT32_MAX) return hipErrorInvalidValue;
     const int CH = E / 8;
     const int swz = (CH >= 8 && (CH & (CH - 1)) == 0) ? 6 : 0;
     float* part = static_cast<float*>(workspace);
