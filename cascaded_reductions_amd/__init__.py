@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16",
-    "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode",
+    "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_segments",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
@@ -44,6 +44,7 @@ _SIGS = {
     "rf_softmax_gemm_fused": ([_c.c_int, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P], _c.c_int),
     "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
+    "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -62,7 +63,7 @@ def load():
         for name, (args, res) in _SIGS.items():
             fn = getattr(lib, name)
             fn.argtypes, fn.restype = args, res
-        if lib.rf_abi_version() != 1:
+        if lib.rf_abi_version() != 2:
             raise RFError(-1, f"unexpected ABI version {lib.rf_abi_version()}")
         _lib = lib
     return _lib
@@ -177,9 +178,21 @@ def segment_merge(part_m, part_s, part_o, out_dtype=None, *, out=None, lse=None,
     return out, lse
 
 
-def attn_decode(q, k, v, nseg: int, scale: float | None = None, out_dtype=None):
-    """Split + merge on the current stream: returns (o [B,H,D], lse [B,H])."""
+def attn_decode_segments(rows: int, L: int, num_cus: int = 0) -> int:
+    """The library's segment count for rows = B*H decode rows over L keys (rf_attn_decode_segments);
+    num_cus <= 0 asks the current device."""
+    n = int(load().rf_attn_decode_segments(int(rows), int(L), int(num_cus)))
+    if n <= 0:
+        raise RFError(1, load().rf_last_error().decode())
+    return n
+
+
+def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, out_dtype=None):
+    """Split + merge on the current stream: returns (o [B,H,D], lse [B,H]). With nseg None the
+    segment count comes from attn_decode_segments."""
     B, H, D = q.shape
+    if nseg is None:
+        nseg = attn_decode_segments(B * H, k.shape[2])
     pm, ps, po = attn_decode_split(q, k, v, nseg, scale)
     o, lse = segment_merge(pm, ps, po, out_dtype)
     return o.view(B, H, D), lse.view(B, H)

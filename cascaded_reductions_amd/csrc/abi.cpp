@@ -171,6 +171,30 @@ rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int6
     return device_status(e, "rf_attn_decode_split launch");
 }
 
+int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus) {
+    if (rows < 1 || L < 1) {
+        fail(RF_ERR_INVALID_ARGUMENT, "rows and L must be >= 1 (got %lld, %lld)", (long long)rows, (long long)L);
+        return 0;
+    }
+    if (num_cus <= 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        num_cus = n;
+    }
+    constexpr int64_t kMinSegKeys = 128;   // shortest segment worth a wave
+    constexpr int64_t kMaxSeg = 1024;      // the merge kernel's limit
+    const int64_t waves = 4 * num_cus;     // one wave per SIMD
+    int64_t n = rows >= waves ? 1 : (waves + rows - 1) / rows;
+    const int64_t by_len = L / kMinSegKeys > 1 ? L / kMinSegKeys : 1;
+    if (n > by_len) n = by_len;
+    if (n > kMaxSeg) n = kMaxSeg;
+    if (n > L) n = L;
+    ok();
+    return n;
+}
+
 rf_status rf_segment_merge(const float* part_m, const float* part_s, const float* part_o,
                            int64_t rows, int64_t nseg, int64_t D, rf_dtype out_dt, void* o,
                            float* lse, rf_stream stream) {

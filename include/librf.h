@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 1
+#define RF_ABI_VERSION 2
 
 /* Exported symbols (the library is built with hidden visibility by default). */
 #if defined(__GNUC__) || defined(__clang__)
@@ -121,6 +121,26 @@ RF_API rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k
 RF_API rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int64_t B,
                                int64_t H, int64_t L, int64_t D, int64_t nseg, float scale,
                                float* part_m, float* part_s, float* part_o, rf_stream stream);
+
+/*
+ * rf_attn_decode_segments -- segment count for rf_attn_decode_split.
+ *
+ * A host-side rule (no device work) for how finely to split the key axis. The
+ * explainer's section 5.2 asks for a launch whose waves per compute unit are
+ * close to a whole number, and its sections 5.3 and 6 for enough parallelism
+ * on long sequences (split the key axis). The split kernel streams each
+ * segment with one wave and saturates HBM once every SIMD runs one wave, so
+ * the rule asks for the fewest segments that give rows * nseg >= 4 * num_cus
+ * waves (one per SIMD, a whole number of waves per compute unit), with
+ * segments of at least 128 keys; more segments only add partial traffic and
+ * merge work.
+ *
+ *   rows     B * H query rows (>= 1).   L  keys per row (>= 1).
+ *   num_cus  compute units of the device (256 on MI355X); <= 0 queries the
+ *            current HIP device.
+ *   Returns  nseg in [1, min(L, 1024)], or 0 if rows or L < 1 (see rf_last_error).
+ */
+RF_API int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus);
 
 /*
  * rf_segment_merge -- merge of per-segment (max, sum, partial-O) triples.

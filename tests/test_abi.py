@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused",
-        "rf_attn_decode_split", "rf_segment_merge", "rf_moe_route_workspace_size", "rf_moe_route",
+        "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_moe_route_workspace_size",
+        "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rf_abi_version() == 1
+    assert lib.rf_abi_version() == 2
     for code, name in [(0, b"RF_OK"), (1, b"RF_ERR_INVALID_ARGUMENT"), (2, b"RF_ERR_UNSUPPORTED"),
                        (3, b"RF_ERR_BUFFER_TOO_SMALL"), (4, b"RF_ERR_DEVICE")]:
         assert lib.rf_status_string(code) == name
@@ -145,3 +146,28 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         rf.softmax_gemm_fused(q, q, q)
+
+
+def test_decode_segment_rule(lib):
+    """One wave per SIMD (rows * nseg >= 4 * CUs) with the fewest segments, segments of at
+    least 128 keys, at most 1024 segments."""
+    seg = lib.rf_attn_decode_segments
+    assert seg(1024, 2048, 256) == 1          # 32 x 32 heads already fill every SIMD
+    assert seg(1024, 16384, 256) == 1
+    assert seg(4096, 512, 256) == 1
+    assert seg(256, 2048, 256) == 4           # 8 x 32 heads: 4 segments -> 1024 waves
+    assert seg(32, 131072, 256) == 32
+    assert seg(300, 4096, 256) == 4           # ceil(1024 / 300)
+    assert seg(256, 256, 256) == 2            # capped by 128-key segments
+    assert seg(1, 100, 256) == 1
+    assert seg(1, 10 ** 6, 256) == 1024       # the merge's limit
+    assert seg(8, 300, 304) == 2
+    for rows in (1, 3, 64, 255, 1000):
+        for L in (1, 127, 128, 5000, 70000):
+            n = seg(rows, L, 256)
+            assert 1 <= n <= min(L, 1024)
+            assert n == 1 or L // n >= 128
+            if n < min(1024, max(1, L // 128)):
+                assert rows * n >= 1024 and rows * (n - 1) < 1024
+    assert seg(0, 10, 256) == 0 and b"rows and L" in lib.rf_last_error()
+    assert seg(5, 0, 256) == 0

@@ -95,8 +95,21 @@ def test_deterministic(rf):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("B,H,L,D", [
+    (2, 4, 300, 128),     # 8 rows: two 150-key segments
+    (1, 1, 5000, 64),     # one row: 39 segments of 129 keys
+    (2, 2, 70, 128),      # shorter than one 128-key segment
+    (8, 32, 2048, 128),   # 256 rows: four segments
+])
+def test_automatic_segment_count(rf, B, H, L, D):
+    """rf_attn_decode_segments' choice goes through the same split + merge."""
+    nseg = rf.attn_decode_segments(B * H, L)
+    assert 1 <= nseg <= min(L, 1024)
+    _check_case(rf, B, H, L, D, nseg, seed=40 + L)
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("nseg", [8, 32])
+@pytest.mark.parametrize("nseg", [8, 32, None])
 def test_decode_l2048_full(rf, nseg):
     """The L = 2048 workload (32 x 32 heads, D = 128) checked on every head."""
     c = CONFIGS["C3a"]
@@ -113,7 +126,8 @@ def test_decode_l2048_full(rf, nseg):
 
 
 @pytest.mark.slow
-def test_decode_l16384_sampled(rf):
+@pytest.mark.parametrize("nseg", [32, None])
+def test_decode_l16384_sampled(rf, nseg):
     """The L = 16384 workload (8 GiB of K/V): every head computed, 24 heads checked
     against the oracle regenerated slice by slice; 64-bit offsets are exercised."""
     c = CONFIGS["C3b"]
@@ -121,7 +135,7 @@ def test_decode_l16384_sampled(rf):
     q, k, v, scale = decode_inputs(B, H, L, D, c["seed"])
     dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     del k, v
-    o, lse = rf.attn_decode(dq, dk, dv, 32, scale)
+    o, lse = rf.attn_decode(dq, dk, dv, nseg, scale)
     torch.cuda.synchronize()
     go, gl = host(o), host(lse)
     g = np.random.default_rng(7)
