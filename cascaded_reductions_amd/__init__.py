@@ -13,7 +13,7 @@ import math
 import os
 
 __all__ = [
-    "RFError", "load", "lib_path", "RF_F32", "RF_BF16",
+    "RFError", "load", "lib_path", "RF_F32", "RF_BF16", "RF_ATTN_AUTO", "RF_ATTN_INCREMENTAL", "RF_ATTN_WHOLE_ROW",
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_segments",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
@@ -42,6 +42,8 @@ _SIGS = {
     "rf_status_string": ([_c.c_int], _c.c_char_p),
     "rf_last_error": ([], _c.c_char_p),
     "rf_softmax_gemm_fused": ([_c.c_int, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P], _c.c_int),
+    "rf_softmax_gemm_fused_mode": ([_c.c_int, _c.c_int, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P],
+                                   _c.c_int),
     "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
@@ -105,10 +107,19 @@ def _stream(t):
 # ------------------------------------------------------------------ attention
 
 
-def softmax_gemm_fused(q, k, v, scale: float | None = None, *, out=None, lse=None, return_lse: bool = True):
+RF_ATTN_AUTO, RF_ATTN_INCREMENTAL, RF_ATTN_WHOLE_ROW = 0, 1, 2
+_MODES = {"auto": RF_ATTN_AUTO, "incremental": RF_ATTN_INCREMENTAL, "whole_row": RF_ATTN_WHOLE_ROW}
+
+
+def softmax_gemm_fused(q, k, v, scale: float | None = None, *, out=None, lse=None, return_lse: bool = True,
+                       mode: str = "auto"):
     """O = softmax(scale * Q K^T) V for q [B,H,Sq,D], k/v [B,H,Sk,D] (fp32 or bf16).
 
-    Returns (o, lse) with lse [B,H,Sq] fp32 (None if return_lse is False and no lse is given)."""
+    mode: "auto" (whole-row below 256 keys for bf16, else incremental), "incremental" or
+    "whole_row" (bf16, Sk <= 256). Returns (o, lse) with lse [B,H,Sq] fp32 (None if
+    return_lse is False and no lse is given)."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
     torch = _torch()
     dt = q.dtype
     if dt not in (torch.float32, torch.bfloat16):
@@ -129,8 +140,9 @@ def softmax_gemm_fused(q, k, v, scale: float | None = None, *, out=None, lse=Non
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, H, Sq))
-    _check(load().rf_softmax_gemm_fused(RF_F32 if dt == torch.float32 else RF_BF16, _ptr(q), _ptr(k), _ptr(v),
-                                        _ptr(out), _ptr(lse), B, H, Sq, Sk, D, float(scale), _stream(q)))
+    _check(load().rf_softmax_gemm_fused_mode(_MODES[mode], RF_F32 if dt == torch.float32 else RF_BF16, _ptr(q),
+                                             _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, float(scale),
+                                             _stream(q)))
     return out, lse
 
 

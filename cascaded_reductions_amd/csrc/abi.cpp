@@ -101,6 +101,14 @@ const char* rf_last_error(void) { return t_err.c_str(); }
 rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const void* v,
                                 void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
                                 int64_t Sk, int64_t D, float scale, rf_stream stream) {
+    return rf_softmax_gemm_fused_mode(RF_ATTN_AUTO, dt, q, k, v, o, lse, B, H, Sq, Sk, D, scale, stream);
+}
+
+rf_status rf_softmax_gemm_fused_mode(rf_attn_mode mode, rf_dtype dt, const void* q, const void* k,
+                                     const void* v, void* o, float* lse, int64_t B, int64_t H,
+                                     int64_t Sq, int64_t Sk, int64_t D, float scale, rf_stream stream) {
+    RF_REQUIRE(mode == RF_ATTN_AUTO || mode == RF_ATTN_INCREMENTAL || mode == RF_ATTN_WHOLE_ROW,
+               RF_ERR_INVALID_ARGUMENT, "mode must be RF_ATTN_AUTO, RF_ATTN_INCREMENTAL or RF_ATTN_WHOLE_ROW");
     RF_REQUIRE(dt == RF_F32 || dt == RF_BF16, RF_ERR_INVALID_ARGUMENT, "dt must be RF_F32 or RF_BF16");
     RF_PTR(q, "q");
     RF_PTR(k, "k");
@@ -125,9 +133,20 @@ rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k, const
                    !overlap(lse, nl * 4, k, nk * es) && !overlap(lse, nl * 4, v, nk * es) &&
                    !overlap(lse, nl * 4, o, nq * es),
                RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    RF_REQUIRE(mode != RF_ATTN_WHOLE_ROW || (dt == RF_BF16 && Sk <= rf::kWholeRowMaxKeys), RF_ERR_UNSUPPORTED,
+               "RF_ATTN_WHOLE_ROW needs RF_BF16 and Sk <= %lld (got Sk=%lld)", (long long)rf::kWholeRowMaxKeys,
+               (long long)Sk);
+    // The automatic choice takes the explainer's threshold (whole-row below 256 keys) except
+    // where the whole-row kernel measured slower on MI355X: D = 64 rows of 8 tiles (225..255 keys).
+    const bool auto_whole = Sk < 256 && (D == 128 || Sk <= 224);
+    const bool whole = dt == RF_BF16 && (mode == RF_ATTN_WHOLE_ROW || (mode == RF_ATTN_AUTO && auto_whole));
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (dt == RF_F32)
+    if (whole)
+        e = rf::launch_attn_whole_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B * H, Sq,
+                                       Sk, int(D), scale, s);
+    else if (dt == RF_F32)
         e = rf::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<float*>(o), lse,
                                     B * H, Sq, Sk, int(D), scale, s);

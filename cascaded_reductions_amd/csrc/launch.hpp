@@ -16,6 +16,11 @@ hipError_t launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint
                                 uint16_t* o, float* lse, int64_t BH, int64_t Sq, int64_t Sk,
                                 int D, float scale, hipStream_t stream);
 
+// Whole-row (non-incremental) bf16 attention for short key axes, 1 <= Sk <= kWholeRowMaxKeys.
+constexpr int64_t kWholeRowMaxKeys = 256;
+hipError_t launch_attn_whole_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                                  int64_t BH, int64_t Sq, int64_t Sk, int D, float scale, hipStream_t stream);
+
 // Multi-segment decode split: q [R, D], k/v [R, L, D] bf16, R = B*H rows.
 hipError_t launch_decode_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t R, int64_t L, int D, int64_t nseg, float scale,
@@ -27,7 +32,7 @@ hipError_t launch_segment_merge(const float* part_m, const float* part_s, const 
                                 float* lse, hipStream_t stream);
 
 // MoE gate: x [T, Hd] bf16, w [Hd, E] bf16 -> idx/w [T, k], optional scores [T, E].
-// The workspace holds per-token-block counters and partial score blocks.
+// The workspace holds the partial score blocks of the hidden ranges.
 size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E);
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd,
                             int E, int k, int32_t* idx, float* w, float* scores, void* workspace,

@@ -100,6 +100,33 @@ RF_API rf_status rf_softmax_gemm_fused(rf_dtype dt, const void* q, const void* k
                                 void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
                                 int64_t Sk, int64_t D, float scale, rf_stream stream);
 
+/* How rf_softmax_gemm_fused_mode evaluates the cascade. */
+typedef enum rf_attn_mode {
+    RF_ATTN_AUTO = 0,        /* whole-row for bf16 rows shorter than 256 keys (D = 64: at most
+                                224), else incremental                                         */
+    RF_ATTN_INCREMENTAL = 1, /* running maximum, rescaled running sum and accumulator           */
+    RF_ATTN_WHOLE_ROW = 2    /* every score of a row on chip, the exact maximum, no rescaling   */
+} rf_attn_mode;
+
+/*
+ * rf_softmax_gemm_fused_mode -- rf_softmax_gemm_fused with the evaluation chosen
+ * explicitly. The explainer's section 5.2 recommends the non-incremental form for
+ * sequences shorter than 256 and the incremental form from 256 on; RF_ATTN_AUTO
+ * applies that threshold, except that D = 64 rows of more than 224 keys stay
+ * incremental (the whole-row kernel measured slower there on MI355X).
+ * rf_softmax_gemm_fused is RF_ATTN_AUTO. The whole-row
+ * form keeps the head's entire K and V in LDS and every score of the row block in
+ * registers, then takes the exact maximum, the exponentials, their sum and P V
+ * (the three passes of the explainer's section 2.1, on chip).
+ *
+ *   mode   RF_ATTN_AUTO, RF_ATTN_INCREMENTAL or RF_ATTN_WHOLE_ROW.
+ *   Other arguments as for rf_softmax_gemm_fused.
+ *   RF_ATTN_WHOLE_ROW supports RF_BF16 with 1 <= Sk <= 256 (RF_ERR_UNSUPPORTED otherwise).
+ */
+RF_API rf_status rf_softmax_gemm_fused_mode(rf_attn_mode mode, rf_dtype dt, const void* q, const void* k,
+                                     const void* v, void* o, float* lse, int64_t B, int64_t H,
+                                     int64_t Sq, int64_t Sk, int64_t D, float scale, rf_stream stream);
+
 /*
  * rf_attn_decode_split -- multi-segment decode attention, first kernel of two.
  *

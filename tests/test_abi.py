@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused",
+        "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
         "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_moe_route_workspace_size",
         "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
@@ -171,3 +171,13 @@ def test_decode_segment_rule(lib):
                 assert rows * n >= 1024 and rows * (n - 1) < 1024
     assert seg(0, 10, 256) == 0 and b"rows and L" in lib.rf_last_error()
     assert seg(5, 0, 256) == 0
+
+
+def test_attention_mode_validation(lib):
+    m = lib.rf_softmax_gemm_fused_mode
+    args = (P, P2, P3, P4, None, 1, 1, 4, 4, 64, 0.125, None)
+    assert m(3, 1, *args) == INVALID and b"mode" in lib.rf_last_error()
+    assert m(2, 0, *args) == UNSUPPORTED and b"RF_ATTN_WHOLE_ROW" in lib.rf_last_error()   # fp32
+    long_args = (P, P2, P3, P4, None, 1, 1, 4, 257, 64, 0.125, None)
+    assert m(2, 1, *long_args) == UNSUPPORTED                                               # Sk > 256
+    assert m(1, 1, P, None, P3, P4, None, 1, 1, 4, 4, 64, 0.125, None) == INVALID           # k NULL

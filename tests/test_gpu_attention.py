@@ -153,3 +153,46 @@ def test_bf16_stepped_scores(rf):
     ro, rl = _ref(inp)
     assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
     assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+# ------------------------------------------------------------------ whole-row (non-incremental) form
+
+
+def _run_mode(rf, inp, mode):
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    o, lse = rf.softmax_gemm_fused(q, k, v, inp.scale, mode=mode)
+    import torch
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,scale", [
+    (1, 2, 64, 1, 64, 0.125),         # a single key
+    (2, 3, 100, 17, 64, 0.125),       # one partial tile, ragged query blocks
+    (1, 2, 130, 32, 128, 0.0883883),  # exactly one tile, D = 128
+    (2, 2, 77, 33, 64, 1.0),          # two tiles, the second with one key
+    (1, 1, 128, 200, 128, 0.0883883), # seven tiles, D = 128
+    (2, 1, 40, 255, 64, 3.0),         # large scores
+    (1, 2, 300, 256, 64, 0.125),      # the longest row the form takes
+    (1, 1, 64, 96, 64, -0.125),       # negative scale
+    (1, 1, 64, 70, 64, 0.0),          # scale 0: the mean of V
+])
+def test_bf16_whole_row(rf, B, H, Sq, Sk, D, scale):
+    inp = attn_inputs(B, H, Sq, Sk, D, "bf16", seed=700 + Sq + Sk, scale=scale)
+    o, lse = _run_mode(rf, inp, "whole_row")
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
+
+
+def test_bf16_modes_agree_below_threshold(rf):
+    """Below 256 keys the automatic choice is the whole-row form; both forms match the oracle."""
+    inp = attn_inputs(2, 4, 256, 192, 64, "bf16", seed=77, scale=0.125)
+    ro, rl = _ref(inp)
+    for mode in ("auto", "whole_row", "incremental"):
+        o, lse = _run_mode(rf, inp, mode)
+        assert_close(o, ro, BF16_ATOL, BF16_RTOL, f"O ({mode})")
+        assert_close(lse, rl, BF16_ATOL, BF16_RTOL, f"lse ({mode})")
+    a, _ = _run_mode(rf, inp, "auto")
+    w, _ = _run_mode(rf, inp, "whole_row")
+    assert np.array_equal(a, w)
