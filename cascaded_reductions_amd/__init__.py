@@ -15,6 +15,7 @@ import os
 __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16", "RF_ATTN_AUTO", "RF_ATTN_INCREMENTAL", "RF_ATTN_WHOLE_ROW",
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_segments",
+    "mla_decode_split", "mla_decode",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
@@ -47,6 +48,7 @@ _SIGS = {
     "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
+    "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -208,6 +210,42 @@ def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, ou
     pm, ps, po = attn_decode_split(q, k, v, nseg, scale)
     o, lse = segment_merge(pm, ps, po, out_dtype)
     return o.view(B, H, D), lse.view(B, H)
+
+
+# ------------------------------------------------------------------ MLA decode
+
+MLA_DQK, MLA_DV = 576, 512
+
+
+def mla_decode_split(q, kv, nseg: int, scale: float, *, part_m=None, part_s=None, part_o=None):
+    """Per-segment partials of MLA decode for q [B,H,576], kv [B,L,576] bf16 (value = the first
+    512 entries of each row). Returns (part_m [B*H,nseg], part_s [B*H,nseg], part_o [B*H,nseg,512])."""
+    torch = _torch()
+    B, H, Dq = q.shape
+    L = kv.shape[1]
+    _need(q, "q", torch.bfloat16, (B, H, MLA_DQK))
+    _need(kv, "kv", torch.bfloat16, (B, L, MLA_DQK))
+    dev = q.device
+    part_m = torch.empty((B * H, nseg), dtype=torch.float32, device=dev) if part_m is None else part_m
+    part_s = torch.empty((B * H, nseg), dtype=torch.float32, device=dev) if part_s is None else part_s
+    part_o = torch.empty((B * H, nseg, MLA_DV), dtype=torch.float32, device=dev) if part_o is None else part_o
+    _need(part_m, "part_m", torch.float32, (B * H, nseg))
+    _need(part_s, "part_s", torch.float32, (B * H, nseg))
+    _need(part_o, "part_o", torch.float32, (B * H, nseg, MLA_DV))
+    _check(load().rf_mla_decode_split(_ptr(q), _ptr(kv), B, H, L, MLA_DQK, MLA_DV, nseg, float(scale),
+                                      _ptr(part_m), _ptr(part_s), _ptr(part_o), _stream(q)))
+    return part_m, part_s, part_o
+
+
+def mla_decode(q, kv, scale: float, nseg: int | None = None, out_dtype=None):
+    """Split + merge: returns (o [B,H,512], lse [B,H]). With nseg None, the segment rule of
+    attn_decode_segments counts the split kernel's waves (four per 64 heads)."""
+    B, H, _ = q.shape
+    if nseg is None:
+        nseg = attn_decode_segments(max(1, B * H // 16), kv.shape[1])
+    pm, ps, po = mla_decode_split(q, kv, nseg, scale)
+    o, lse = segment_merge(pm, ps, po, out_dtype)
+    return o.view(B, H, MLA_DV), lse.view(B, H)
 
 
 # ------------------------------------------------------------------ MoE gate

@@ -190,6 +190,38 @@ rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int6
     return device_status(e, "rf_attn_decode_split launch");
 }
 
+rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t H, int64_t L, int64_t d_qk,
+                              int64_t d_v, int64_t nseg, float scale, float* part_m, float* part_s,
+                              float* part_o, rf_stream stream) {
+    RF_PTR(q, "q");
+    RF_PTR(kv, "kv");
+    RF_PTR(part_m, "part_m");
+    RF_PTR(part_s, "part_s");
+    RF_PTR(part_o, "part_o");
+    RF_REQUIRE(B >= 1 && H >= 1 && L >= 1, RF_ERR_INVALID_ARGUMENT, "B, H and L must be >= 1");
+    RF_REQUIRE(d_qk == 576 && d_v == 512, RF_ERR_UNSUPPORTED, "d_qk must be 576 and d_v 512 (got %lld, %lld)",
+               (long long)d_qk, (long long)d_v);
+    RF_REQUIRE(H % 32 == 0, RF_ERR_UNSUPPORTED, "H must be a multiple of 32 (got %lld)", (long long)H);
+    RF_REQUIRE(nseg >= 1 && nseg <= L, RF_ERR_INVALID_ARGUMENT, "nseg must be in [1, L] (got %lld)",
+               (long long)nseg);
+    RF_REQUIRE(scale == scale && scale - scale == 0.0f, RF_ERR_INVALID_ARGUMENT, "scale must be finite");
+    int64_t nq, nkv, np, npo, nblk;
+    RF_REQUIRE(prod({B, H, d_qk}, &nq) && prod({B, L, d_qk}, &nkv) && nkv < kMaxElems && prod({B, H, nseg}, &np) &&
+                   prod({np, d_v}, &npo) && npo < kMaxElems && prod({B, (H + 127) / 128, nseg}, &nblk) &&
+                   nblk <= INT32_MAX,
+               RF_ERR_UNSUPPORTED, "problem too large");
+    RF_REQUIRE(!overlap(part_m, np * 4, q, nq * 2) && !overlap(part_m, np * 4, kv, nkv * 2) &&
+                   !overlap(part_s, np * 4, q, nq * 2) && !overlap(part_s, np * 4, kv, nkv * 2) &&
+                   !overlap(part_o, npo * 4, q, nq * 2) && !overlap(part_o, npo * 4, kv, nkv * 2) &&
+                   !overlap(part_m, np * 4, part_s, np * 4) && !overlap(part_m, np * 4, part_o, npo * 4) &&
+                   !overlap(part_s, np * 4, part_o, npo * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipError_t e = rf::launch_mla_decode_split(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), B,
+                                               H, L, nseg, scale, part_m, part_s, part_o,
+                                               static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_mla_decode_split launch");
+}
+
 int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus) {
     if (rows < 1 || L < 1) {
         fail(RF_ERR_INVALID_ARGUMENT, "rows and L must be >= 1 (got %lld, %lld)", (long long)rows, (long long)L);
@@ -226,7 +258,8 @@ rf_status rf_segment_merge(const float* part_m, const float* part_s, const float
     RF_REQUIRE(rows >= 1 && nseg >= 1, RF_ERR_INVALID_ARGUMENT, "rows and nseg must be >= 1");
     RF_REQUIRE(nseg <= 1024, RF_ERR_UNSUPPORTED, "nseg must be <= 1024 (got %lld)", (long long)nseg);
     RF_REQUIRE(D >= 1, RF_ERR_INVALID_ARGUMENT, "D must be >= 1");
-    RF_REQUIRE(D == 64 || D == 128, RF_ERR_UNSUPPORTED, "D must be 64 or 128 (got %lld)", (long long)D);
+    RF_REQUIRE(D == 64 || D == 128 || D == 512, RF_ERR_UNSUPPORTED, "D must be 64, 128 or 512 (got %lld)",
+               (long long)D);
     int64_t np, npo, no;
     RF_REQUIRE(prod({rows, nseg}, &np) && np <= INT32_MAX && prod({np, D}, &npo) && prod({rows, D}, &no) &&
                    npo < kMaxElems,

@@ -160,7 +160,16 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
         for (int tt = 0; tt < n; ++tt) {
             const float wt = __shfl(w, tt, 64);
             const float* src = po + int64_t(t0 + tt) * D;
-            if constexpr (PER == 2) {
+            if constexpr (PER % 4 == 0) {
+#pragma unroll
+                for (int i4 = 0; i4 < PER / 4; ++i4) {
+                    const float4 x = *reinterpret_cast<const float4*>(src + 4 * i4);
+                    O[4 * i4 + 0] = fmaf(wt, x.x, O[4 * i4 + 0]);
+                    O[4 * i4 + 1] = fmaf(wt, x.y, O[4 * i4 + 1]);
+                    O[4 * i4 + 2] = fmaf(wt, x.z, O[4 * i4 + 2]);
+                    O[4 * i4 + 3] = fmaf(wt, x.w, O[4 * i4 + 3]);
+                }
+            } else if constexpr (PER == 2) {
                 const float2 x = *reinterpret_cast<const float2*>(src);
                 O[0] = fmaf(wt, x.x, O[0]);
                 O[1] = fmaf(wt, x.y, O[1]);
@@ -207,7 +216,10 @@ hipError_t launch_segment_merge(const float* part_m, const float* part_s, const 
                                 hipStream_t stream) {
     const int64_t blocks = ceil_div(rows, 4);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    if (D == 128)
+    if (D == 512)
+        hipLaunchKernelGGL(segment_merge_kernel<512>, dim3(unsigned(blocks)), dim3(256), 0, stream, part_m, part_s,
+                           part_o, rows, int(nseg), int(out_bf16), o, lse);
+    else if (D == 128)
         hipLaunchKernelGGL(segment_merge_kernel<128>, dim3(unsigned(blocks)), dim3(256), 0, stream, part_m, part_s,
                            part_o, rows, int(nseg), int(out_bf16), o, lse);
     else

@@ -26,6 +26,12 @@ hipError_t launch_decode_split(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t R, int64_t L, int D, int64_t nseg, float scale,
                                float* part_m, float* part_s, float* part_o, hipStream_t stream);
 
+// Multi-head latent attention decode split: q [B, H, 576], kv [B, L, 576] bf16 (value = the
+// first 512 entries of each cache row); partials for rows b * H + h, D = 512.
+hipError_t launch_mla_decode_split(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t H, int64_t L,
+                                   int64_t nseg, float scale, float* part_m, float* part_s, float* part_o,
+                                   hipStream_t stream);
+
 // Merge of per-segment partials into o [rows, D] (fp32 or bf16) and lse.
 hipError_t launch_segment_merge(const float* part_m, const float* part_s, const float* part_o,
                                 int64_t rows, int64_t nseg, int D, bool out_bf16, void* o,

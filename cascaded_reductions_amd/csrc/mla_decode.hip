@@ -1,0 +1,267 @@
+// Multi-head latent attention (MLA) decode: the multi-segment split kernel.
+//
+// MLA (named among the workloads of the technical summary "RedFuser: An
+// Automatic Operator Fusion Framework for Cascaded Reductions on AI
+// Accelerators", Resultaten) caches one compressed latent per token: a row of
+// DQK = 576 values whose first DV = 512 are the latent c_kv and whose last 64
+// are the shared rotary key. With the key projection absorbed into the query,
+// every head h scores token j as x_hj = scale * <q_h, row_j> (576 values) and
+// reads back o_h = sum_j softmax_j(x_hj) row_j[0 .. 512). It is the softmax ->
+// GEMM cascade of the explainer "RedFuser框架：AI加速器中的算子融合技术解析"
+// (section 4.1) with all heads sharing one key/value row, evaluated per key
+// segment in the incremental form (Multi-Segment strategy, Methodologie 3);
+// the segments are combined by rf_segment_merge (D = 512).
+//
+// Because the heads share the cache row, the per-token work is a small GEMM
+// and runs on the matrix cores: a workgroup owns one batch entry, 64 heads and
+// one key segment, and walks the segment in tiles of 32 tokens staged in LDS (a
+// 3-slot ring filled by direct global-to-LDS loads two tiles ahead). Its four
+// waves are two head blocks of 32 x two halves: half e of a head block forms the
+// scores over key values [288 e, 288 e + 288) and the output over latent values
+// [256 e, 256 e + 256), so a wave holds half of Q (72 registers) and half of the
+// accumulator (128). Per tile and wave:
+//   * partial S^T (32 tokens x 32 heads) = K Q^T on v_mfma_f32_32x32x16_bf16,
+//     18 K-steps; the two halves swap partial scores through LDS and add them
+//     (a + b = b + a exactly, so both hold identical scores and take identical
+//     decisions below);
+//   * the probabilities, packed to bf16, are the B operand of O^T += V^T P^T
+//     (8 blocks of 32 latent values; V^T read with ds_read_b64_tr_b16), and the
+//     row sum is taken from the same packed values;
+//   * the reference maximum is lazy, as in the prefill kernel: a lane whose tile
+//     probabilities sum to at most 2^8 needs no rescale; otherwise the exact row
+//     maximum moves the reference (first tile included).
+// Partials: part_m holds each segment's reference in natural units, part_s and
+// part_o the sum and the unnormalised accumulator relative to it -- the same
+// triple the merge combines exactly whatever the reference is.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rf {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int DQK = 576;                 // latent + rotary key width
+constexpr int DV = 512;                  // latent width (the value)
+constexpr int KT = 32;                   // tokens per tile
+constexpr int RCH = DQK / 8;             // 16-byte chunks per cache row (72)
+constexpr int TILE_CHUNKS = KT * RCH;    // 2304
+constexpr int TILE_ELEMS = KT * DQK;     // 18432 bf16 = 36 KiB
+constexpr int NCQ = DQK / 32;            // K=16 steps of one half's partial scores (18)
+constexpr int DBV = DV / 64;             // 32-wide latent blocks of one half's output (8)
+constexpr int STAGES = 3;
+constexpr int NW = 4;                    // waves: 2 head blocks x 2 halves
+constexpr int HPW = 64;                  // heads per workgroup
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    bf16x2_t t = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, t);
+}
+
+__device__ __forceinline__ bf16x4_t read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+}
+
+// Element offset of logical 8-element chunk c of token row r inside a tile: the chunk
+// index is XOR-swizzled with r & 7 (it stays inside its aligned group of 8 chunks).
+__device__ __forceinline__ int tile_off(int r, int c) { return r * DQK + ((c ^ (r & 7)) << 3); }
+
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t H, int64_t L,
+                      int64_t nseg, int64_t seglen, int nhb, float sl2, uint32_t qsign, float* __restrict__ part_m,
+                      float* __restrict__ part_s, float* __restrict__ part_o) {
+    constexpr int WLT = TILE_CHUNKS / 64 / NW;   // wave loads per tile and wave
+    __shared__ __attribute__((aligned(16))) uint16_t ring[STAGES * TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) float xbuf[NW][16][64];   // partial scores, [reg][lane]
+
+    // Workgroup -> (batch b, head block hb, segment t).
+    const int64_t bid = blockIdx.x;
+    const int64_t t = bid % nseg;
+    const int64_t rest = bid / nseg;
+    const int64_t hb = rest % nhb;
+    const int64_t b = rest / nhb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int blk = wave >> 1;               // head block (32 heads)
+    const int half = wave & 1;               // key/latent half
+
+    const int64_t s0 = t * seglen;
+    const int64_t s1 = s0 + seglen < L ? s0 + seglen : L;
+    const int ntiles = s1 > s0 ? int((s1 - s0 + KT - 1) / KT) : 0;
+    const uint16_t* kvb = kv + b * L * DQK;
+
+    // Tile j of the segment into ring slot `slot`: wave load i (i = wave + NW * w) covers
+    // physical chunks [64 i, 64 i + 64) of the tile; tokens past the segment re-read its
+    // last token (their scores are masked).
+    auto issue = [&](int j, int slot) {
+        const int64_t k0 = s0 + int64_t(j) * KT;
+#pragma unroll
+        for (int w = 0; w < WLT; ++w) {
+            const int i = wave + NW * w;
+            const int p = i * 64 + lane;
+            const int r = p / RCH;
+            const int pc = p - r * RCH;
+            const int lc = pc ^ (r & 7);
+            int64_t key = k0 + r;
+            key = key < s1 ? key : s1 - 1;
+            lds_dma16(kvb + key * DQK + lc * 8, ring + slot * TILE_ELEMS + i * 512);
+        }
+    };
+
+    // Q^T operand: lane (head l32 of the block, lane half h) holds
+    // Q[head][288 half + 16c + 8h .. +7].
+    const int64_t head = hb * HPW + 32 * blk + l32;
+    bf16x8 qf[NCQ];
+    {
+        const int64_t hq = head < H ? head : H - 1;
+        const uint16_t* src = q + (b * H + hq) * DQK + 288 * half + 8 * h;
+#pragma unroll
+        for (int c = 0; c < NCQ; ++c) {
+            u32x4 v4 = *reinterpret_cast<const u32x4*>(src + 16 * c);
+            v4 ^= qsign;
+            qf[c] = __builtin_bit_cast(bf16x8, v4);
+        }
+    }
+
+    f32x16 acc_o[DBV];
+#pragma unroll
+    for (int d = 0; d < DBV; ++d) acc_o[d] = f32x16{};
+    float m_ref = kNegInf, s_part = 0.f;
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+
+    // p = 2^(x sl2 - ref) for the 16 scores of the lane, packed to bf16; masked tokens
+    // (at or past kvalid) get 0. Returns the lane's sum of the packed values.
+    auto probs = [&](const f32x16& sc, int kvalid, uint32_t (&pk)[8]) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            float p0 = exp2_fast(fmaf(sc[r], sl2, -m_ref));
+            float p1 = exp2_fast(fmaf(sc[r + 1], sl2, -m_ref));
+            const int key = (r >> 2) * 8 + 4 * h + (r & 3);
+            p0 = key < kvalid ? p0 : 0.f;
+            p1 = key + 1 < kvalid ? p1 : 0.f;
+            const uint32_t w = pack2(p0, p1);
+            pk[r >> 1] = w;
+            if (r & 2) t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, t1, false);
+            else t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, t0, false);
+        }
+        return t0 + t1;
+    };
+
+    const int j16 = lane & 15;
+    if (ntiles > 0) issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+    for (int j = 0; j < ntiles; ++j) {
+        const int slot = j % STAGES;
+        if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");   // tile j is in
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                       // every wave's part of tile j; tile j - 1 retired
+        if (j + 2 < ntiles) issue(j + 2, (j + 2) % STAGES);
+        const uint16_t* tl = ring + slot * TILE_ELEMS;
+
+        // Partial S^T = K Q^T over this half's 288 key values, then the partner's half.
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NCQ; ++c) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + h));
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[c], sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xbuf[wave][r][lane] = sc[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] += xbuf[wave ^ 1][r][lane];
+        const int64_t kleft = s1 - (s0 + int64_t(j) * KT);
+        const int kvalid = kleft < KT ? int(kleft) : KT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = (r >> 2) * 8 + 4 * h + (r & 3);
+            if (key >= kvalid) sc[r] = kNegInf;
+        }
+
+        uint32_t pk[8];
+        float tsum = probs(sc, kvalid, pk);
+        if (__any(!(tsum <= 256.f))) {         // exact path: row maximum, maybe a new reference
+            float mx = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            const float mx2 = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+            if (mx2 > m_ref) {
+                const float alpha = exp2_fast(m_ref - mx2);   // 0 on the first tile
+                s_part *= alpha;
+#pragma unroll
+                for (int d = 0; d < DBV; ++d) acc_o[d] *= alpha;
+                m_ref = mx2;
+            }
+            tsum = probs(sc, kvalid, pk);
+        }
+        s_part += tsum;
+
+        // O^T += V^T P^T over the tile's two 16-token chunks.
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const u32x4 pb = {pk[kc * 4 + 0], pk[kc * 4 + 1], pk[kc * 4 + 2], pk[kc * 4 + 3]};
+            const int key0 = kc * 16 + 4 * h + (j16 >> 2);
+            const int key1 = key0 + 8;
+#pragma unroll
+            for (int d = 0; d < DBV; ++d) {
+                // 16-lane group: tokens key0 (key1), latent columns 256 half + 32d + 16 (l32/16) + 4 (j%4) .. +3.
+                const int col = 256 * half + 32 * d + 16 * (l32 >> 4) + 4 * (j16 & 3);
+                const bf16x4_t lo = read_tr16(tl + tile_off(key0, col >> 3) + (col & 7));
+                const bf16x4_t hi = read_tr16(tl + tile_off(key1, col >> 3) + (col & 7));
+                const bf16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                    __builtin_bit_cast(bf16x8, pb), acc_o[d], 0, 0, 0);
+            }
+        }
+    }
+
+    // Partials of (row = b * H + head, segment t); both halves hold the same m and s.
+    const float s_row = s_part + __shfl_xor(s_part, 32, 64);
+    if (head < H) {
+        const int64_t pr = (b * H + head) * nseg + t;
+        if (h == 0 && half == 0) {
+            part_m[pr] = m_ref == kNegInf ? kNegInf : m_ref * kLn2;
+            part_s[pr] = s_row;
+        }
+        float* po = part_o + pr * DV + 256 * half;
+#pragma unroll
+        for (int d = 0; d < DBV; ++d)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                // acc_o[d][4 g4 + e] = O^T[32 d + 8 g4 + 4 h + e][head].
+                const float4 w = make_float4(acc_o[d][4 * g4], acc_o[d][4 * g4 + 1], acc_o[d][4 * g4 + 2],
+                                             acc_o[d][4 * g4 + 3]);
+                *reinterpret_cast<float4*>(po + 32 * d + 8 * g4 + 4 * h) = w;
+            }
+    }
+}
+
+hipError_t launch_blocks(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t H, int64_t L, int64_t nseg,
+                        float scale, float* part_m, float* part_s, float* part_o, hipStream_t stream) {
+    const int64_t nhb = ceil_div(H, int64_t(HPW));
+    const int64_t blocks = B * nhb * nseg;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t seglen = ceil_div(L, nseg);
+    const float sl2 = (scale < 0.f ? -scale : scale) * kLog2e;
+    const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+    hipLaunchKernelGGL(mla_split_kernel, dim3(unsigned(blocks)), dim3(NW * 64), 0, stream, q, kv, H, L, nseg, seglen,
+                       int(nhb), sl2, qsign, part_m, part_s, part_o);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mla_decode_split(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t H, int64_t L,
+                                   int64_t nseg, float scale, float* part_m, float* part_s, float* part_o,
+                                   hipStream_t stream) {
+    return launch_blocks(q, kv, B, H, L, nseg, scale, part_m, part_s, part_o, stream);
+}
+
+}  // namespace rf

@@ -181,11 +181,40 @@ RF_API int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus)
  *   part_m, part_s  [rows, nseg] fp32.  part_o  [rows, nseg, D] fp32.
  *   out_dt  RF_F32 or RF_BF16 (RNE): the dtype of o.   o  [rows, D].
  *   lse     [rows] fp32, may be NULL.
- *   Supported: rows >= 1, 1 <= nseg <= 1024, D in {64, 128}.
+ *   Supported: rows >= 1, 1 <= nseg <= 1024, D in {64, 128, 512} (512: the latent
+ *   width of rf_mla_decode_split).
  */
 RF_API rf_status rf_segment_merge(const float* part_m, const float* part_s, const float* part_o,
                            int64_t rows, int64_t nseg, int64_t D, rf_dtype out_dt, void* o,
                            float* lse, rf_stream stream);
+
+/*
+ * rf_mla_decode_split -- multi-head latent attention (MLA) decode, first kernel of two.
+ *
+ * MLA (named among the workloads of the technical summary's "Resultaten") caches
+ * one compressed row per token: d_qk = 576 values, of which the first d_v = 512
+ * are the latent and the rest the shared rotary key. With the key projection
+ * absorbed into the query, head h of batch entry b scores token j as
+ * x_hj = scale * <q[b,h,:], kv[b,j,:]> and reads back sum_j softmax_j(x) kv[b,j,0:d_v]:
+ * the softmax -> GEMM cascade with every head sharing the cache rows. The key
+ * axis is split into nseg segments of ceil(L/nseg) tokens (as in
+ * rf_attn_decode_split); for row r = b*H + h and segment t it writes a triple
+ * that rf_segment_merge (D = 512) combines:
+ *     part_m[r*nseg + t]          a reference value m_t (natural units, -inf if empty),
+ *     part_s[r*nseg + t]          sum_j exp(x_j - m_t),
+ *     part_o[(r*nseg + t)*512 + d] sum_j exp(x_j - m_t) kv[b,j,d]  (unnormalised).
+ * m_t is at most the segment maximum plus 8 ln 2 (a lazily moved reference); the
+ * triple represents the segment exactly whatever m_t is, and the merge result
+ * does not depend on it.
+ *
+ *   q        [B, H, 576] bf16.   kv  [B, L, 576] bf16.
+ *   d_qk, d_v  must be 576 and 512.
+ *   part_m, part_s  fp32, B*H*nseg elements each.  part_o  fp32, B*H*nseg*512 elements.
+ *   Supported: B, H, L >= 1; H a multiple of 32; 1 <= nseg <= L; B*ceil(H/128)*nseg <= 2^31 - 1.
+ */
+RF_API rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t H, int64_t L,
+                                     int64_t d_qk, int64_t d_v, int64_t nseg, float scale, float* part_m,
+                                     float* part_s, float* part_o, rf_stream stream);
 
 /*
  * rf_moe_route_workspace_size -- bytes of device workspace rf_moe_route needs.

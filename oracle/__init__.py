@@ -26,14 +26,14 @@ Every function is pinned by tests that do not re-type its formula (brute force
 on tiny inputs, closed forms, invariants, library cross-checks, exhaustive
 codec checks); no function is "parity unpinned".
 """
-from .attention import attention, attention_incremental, decode, decode_streaming
+from .attention import attention, attention_incremental, decode, decode_streaming, mla_decode
 from .segments import segment_bounds, split_partials, merge_partials, decode_split_merge
 from .moe import moe_route, gate_scores
 from .quant import (E4M3_MAX, e4m3fn_decode, e4m3fn_encode, fl32, quantize_rows,
                     quant_gemm, quant_gemm_acc)
 
 __all__ = [
-    "attention", "attention_incremental", "decode", "decode_streaming",
+    "attention", "attention_incremental", "decode", "decode_streaming", "mla_decode",
     "segment_bounds", "split_partials", "merge_partials", "decode_split_merge",
     "moe_route", "gate_scores",
     "E4M3_MAX", "e4m3fn_decode", "e4m3fn_encode", "fl32", "quantize_rows",

@@ -100,3 +100,14 @@ def decode_streaming(q_bh, kv_of, heads, scale):
         k, v = kv_of(b, h)
         o, lse = attention(_f64(q_bh(b, h))[None, :], k, v, scale)
         yield (b, h), o[0], float(lse[0])
+
+
+def mla_decode(q, kv, d_v, scale):
+    """Multi-head latent attention decode with the key projection absorbed ([summary],
+    Resultaten, names MLA among the attention workloads): every head of batch entry b
+    attends to the same cache rows, the keys are the whole rows and the values their
+    first d_v entries. This is the plain definition above with the heads as the query rows.
+
+    q [B, H, Dk], kv [B, L, Dk] (Dk >= d_v). Returns (o [B, H, d_v], lse [B, H])."""
+    kv = _f64(kv)
+    return attention(_f64(q), kv, kv[..., :d_v], scale)

@@ -119,6 +119,35 @@ def decode_inputs(B: int, H: int, L: int, D: int, seed: int, threads: int | None
     return q, k, v, float(np.float32(1.0 / np.sqrt(D)))
 
 
+# ---------------------------------------------------------------- MLA decode (latent cache)
+
+MLA_DQK, MLA_DV, MLA_QK_HEAD = 576, 512, 192
+
+
+def mla_q(B: int, H: int, seed: int) -> np.ndarray:
+    """Absorbed queries q [B,H,576] bf16 bits from rng(seed, 0)."""
+    return f32_to_bf16_bits(_normal_f32(rng(seed, 0), (B, H, MLA_DQK)))
+
+
+def mla_kv_slice(b: int, L: int, seed: int) -> np.ndarray:
+    """Cache rows kv[b] [L,576] bf16 bits (latent 512 then rotary 64) from rng(seed, 1, b)."""
+    return f32_to_bf16_bits(_normal_f32(rng(seed, 1, b), (L, MLA_DQK)))
+
+
+def mla_inputs(B: int, H: int, L: int, seed: int):
+    """q [B,H,576], kv [B,L,576] (bf16 bits) and the scale fl32(1/sqrt(192)) (the softmax
+    scale of a 128 + 64 query-key head, whose product the absorbed form preserves)."""
+    q = mla_q(B, H, seed)
+    kv = np.empty((B, L, MLA_DQK), np.uint16)
+
+    def fill(b):
+        kv[b] = mla_kv_slice(b, L, seed)
+
+    with _cf.ThreadPoolExecutor(min(16, _os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(B)))
+    return q, kv, float(np.float32(1.0 / np.sqrt(MLA_QK_HEAD)))
+
+
 # ---------------------------------------------------------------- MoE gate
 
 def _near_tie_rows(x_bits: np.ndarray, w_bits: np.ndarray, k: int, gap: float) -> np.ndarray:
@@ -196,4 +225,7 @@ CONFIGS = {
     "C3b": dict(kind="decode", B=32, H=32, L=16384, D=128, seed=4),
     "C4": dict(kind="moe", T=2048, Hd=4096, E=64, k=2, seed=5),
     "C5": dict(kind="quant", M=4096, N=4096, K=4096, seed=6),
+    # Multi-head latent attention decode (a workload beyond the five above): 32 sequences,
+    # 128 heads sharing a 576-wide latent cache of 4096 tokens.
+    "MLA": dict(kind="mla", B=32, H=128, L=4096, seed=7),
 }

@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
-        "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_moe_route_workspace_size",
+        "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split",
+        "rf_moe_route_workspace_size",
         "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
 
@@ -181,3 +182,22 @@ def test_attention_mode_validation(lib):
     long_args = (P, P2, P3, P4, None, 1, 1, 4, 257, 64, 0.125, None)
     assert m(2, 1, *long_args) == UNSUPPORTED                                               # Sk > 256
     assert m(1, 1, P, None, P3, P4, None, 1, 1, 4, 4, 64, 0.125, None) == INVALID           # k NULL
+
+
+def test_mla_validation(lib):
+    m = lib.rf_mla_decode_split
+    ok_args = dict(q=P, kv=P2, B=1, H=64, L=100, dqk=576, dv=512, nseg=2, scale=0.07, pm=P3, ps=P4, po=P5)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return m(a["q"], a["kv"], a["B"], a["H"], a["L"], a["dqk"], a["dv"], a["nseg"], a["scale"], a["pm"], a["ps"],
+                 a["po"], None)
+    assert call(q=None) == INVALID
+    assert call(H=48) == UNSUPPORTED and b"multiple of 32" in lib.rf_last_error()
+    assert call(dqk=512) == UNSUPPORTED
+    assert call(nseg=101) == INVALID
+    assert call(nseg=0) == INVALID
+    assert call(L=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(po=P) == INVALID and b"alias" in lib.rf_last_error()       # part_o over q
+    assert lib.rf_segment_merge(P, P2, P3, 4, 2, 256, 1, P4, None, None) == UNSUPPORTED   # D 256

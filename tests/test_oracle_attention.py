@@ -205,3 +205,43 @@ def test_decode_is_single_query_attention():
         lambda b, h: q[b, h], lambda b, h: (k[b, h], v[b, h]), [(1, 2), (0, 1)], 0.35)}
     np.testing.assert_allclose(streamed[(1, 2)][0], o[1, 2], rtol=0, atol=0)
     assert math.isclose(streamed[(0, 1)][1], lse[0, 1], rel_tol=0, abs_tol=0)
+
+
+def test_mla_decode_brute_force():
+    """MLA decode against a pure-Python loop: keys are whole cache rows, values their first d_v
+    entries, shared by every head (math.fsum, exact exp ratios)."""
+    import math
+    g = np.random.default_rng(11)
+    B, H, L, Dk, dv, scale = 2, 3, 5, 4, 3, 0.7
+    q = g.standard_normal((B, H, Dk))
+    kv = g.standard_normal((B, L, Dk))
+    o, lse = oracle.mla_decode(q, kv, dv, scale)
+    assert o.shape == (B, H, dv) and lse.shape == (B, H)
+    for b in range(B):
+        for h in range(H):
+            x = [float(np.float32(scale)) * math.fsum(q[b, h, d] * kv[b, j, d] for d in range(Dk)) for j in range(L)]
+            m = max(x)
+            e = [math.exp(xi - m) for xi in x]
+            s = math.fsum(e)
+            for d in range(dv):
+                assert abs(o[b, h, d] - math.fsum(e[j] * kv[b, j, d] for j in range(L)) / s) < 1e-12
+            assert abs(lse[b, h] - (m + math.log(s))) < 1e-12
+
+
+def test_mla_decode_rotary_part_only_scores():
+    """The rotary columns (past d_v) only enter the scores: with queries that are zero there,
+    any change to those cache columns leaves O and lse unchanged; with all-zero queries O is
+    the mean latent row and lse = ln L."""
+    g = np.random.default_rng(12)
+    q = g.standard_normal((1, 2, 8))
+    q[..., 5:] = 0.0
+    kv = g.standard_normal((1, 6, 8))
+    o1, l1 = oracle.mla_decode(q, kv, 5, 0.3)
+    kv2 = kv.copy()
+    kv2[..., 5:] = g.standard_normal((1, 6, 3)) * 100.0
+    o2, l2 = oracle.mla_decode(q, kv2, 5, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    o0, lse0 = oracle.mla_decode(np.zeros_like(q), kv, 5, 0.3)
+    np.testing.assert_allclose(o0[0, 0], kv[0, :, :5].mean(axis=0), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse0, np.log(6.0), rtol=1e-14)
