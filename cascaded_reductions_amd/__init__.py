@@ -15,7 +15,7 @@ import os
 __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16", "RF_ATTN_AUTO", "RF_ATTN_INCREMENTAL", "RF_ATTN_WHOLE_ROW",
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_segments",
-    "mla_decode_split", "mla_decode",
+    "mla_decode_split", "mla_decode", "row_cascade",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
@@ -49,6 +49,7 @@ _SIGS = {
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
     "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
+    "rf_row_cascade": ([_c.c_int, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -246,6 +247,32 @@ def mla_decode(q, kv, scale: float, nseg: int | None = None, out_dtype=None):
     pm, ps, po = mla_decode_split(q, kv, nseg, scale)
     o, lse = segment_merge(pm, ps, po, out_dtype)
     return o.view(B, H, MLA_DV), lse.view(B, H)
+
+
+# ------------------------------------------------------------------ generic row cascades
+
+_CASCADES = {"logsumexp": 0, "softmax_weighted": 1, "topk_softmax": 2, "mean_var": 3}
+
+
+def row_cascade(kind: str, x, payload=None, k: int = 0):
+    """One of the library's template cascades over each row of x [R, N] fp32:
+    "logsumexp" -> [R]; "softmax_weighted" (payload [R, N, P]) -> [R, P];
+    "topk_softmax" -> (weights [R, k], indices [R, k] int32); "mean_var" -> [R, 2]."""
+    torch = _torch()
+    if kind not in _CASCADES:
+        raise ValueError(f"kind must be one of {sorted(_CASCADES)}")
+    R, N = x.shape
+    _need(x, "x", torch.float32, (R, N))
+    P = 0
+    if kind == "softmax_weighted":
+        P = payload.shape[2]
+        _need(payload, "payload", torch.float32, (R, N, P))
+    width = {"logsumexp": None, "softmax_weighted": P, "topk_softmax": k, "mean_var": 2}[kind]
+    out = torch.empty((R,) if width is None else (R, width), dtype=torch.float32, device=x.device)
+    idx = torch.empty((R, k), dtype=torch.int32, device=x.device) if kind == "topk_softmax" else None
+    _check(load().rf_row_cascade(_CASCADES[kind], _ptr(x), _ptr(payload) if P else None, R, N, P, k, _ptr(out),
+                                 _ptr(idx), _stream(x)))
+    return (out, idx) if idx is not None else out
 
 
 # ------------------------------------------------------------------ MoE gate

@@ -222,6 +222,40 @@ rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t 
     return device_status(e, "rf_mla_decode_split launch");
 }
 
+rf_status rf_row_cascade(rf_cascade kind, const float* x, const float* payload, int64_t R, int64_t N, int64_t P,
+                         int64_t k, float* out, int32_t* out_idx, rf_stream stream) {
+    RF_REQUIRE(kind >= RF_CASCADE_LOGSUMEXP && kind <= RF_CASCADE_MEAN_VAR, RF_ERR_INVALID_ARGUMENT,
+               "unknown cascade kind %d", int(kind));
+    RF_PTR(x, "x");
+    RF_PTR(out, "out");
+    RF_REQUIRE(R >= 1 && N >= 1, RF_ERR_INVALID_ARGUMENT, "R and N must be >= 1");
+    RF_REQUIRE(N < (int64_t(1) << 31), RF_ERR_UNSUPPORTED, "N must be below 2^31");
+    const bool weighted = kind == RF_CASCADE_SOFTMAX_WEIGHTED, topk = kind == RF_CASCADE_TOPK_SOFTMAX;
+    if (weighted) {
+        RF_PTR(payload, "payload");
+        RF_REQUIRE(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, RF_ERR_UNSUPPORTED,
+                   "P must be 1, 2, 4, 8 or 16 (got %lld)", (long long)P);
+    } else {
+        RF_REQUIRE(P == 0, RF_ERR_INVALID_ARGUMENT, "P must be 0 for this cascade");
+    }
+    if (topk) {
+        RF_PTR(out_idx, "out_idx");
+        RF_REQUIRE(k >= 1 && k <= 8 && k <= N, RF_ERR_UNSUPPORTED, "k must be in [1, min(8, N)] (got %lld)",
+                   (long long)k);
+    }
+    int64_t nx, np = 0, no;
+    const int64_t ow = weighted ? P : topk ? k : kind == RF_CASCADE_MEAN_VAR ? 2 : 1;
+    RF_REQUIRE(prod({R, N}, &nx) && nx < kMaxElems && (!weighted || (prod({nx, P}, &np) && np < kMaxElems)) &&
+                   prod({R, ow}, &no),
+               RF_ERR_UNSUPPORTED, "problem too large");
+    RF_REQUIRE(!overlap(out, no * 4, x, nx * 4) && !overlap(out, no * 4, payload, np * 4) &&
+                   (!topk || (!overlap(out_idx, no * 4, x, nx * 4) && !overlap(out_idx, no * 4, out, no * 4))),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    const hipError_t e = rf::launch_row_cascade(int(kind), x, weighted ? payload : nullptr, R, N, int(P), int(k),
+                                                out, topk ? out_idx : nullptr, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_row_cascade launch");
+}
+
 int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus) {
     if (rows < 1 || L < 1) {
         fail(RF_ERR_INVALID_ARGUMENT, "rows and L must be >= 1 (got %lld, %lld)", (long long)rows, (long long)L);

@@ -32,6 +32,11 @@ hipError_t launch_mla_decode_split(const uint16_t* q, const uint16_t* kv, int64_
                                    int64_t nseg, float scale, float* part_m, float* part_s, float* part_o,
                                    hipStream_t stream);
 
+// Row cascades from the generic incremental template: kind 0 logsumexp, 1 softmax-weighted
+// sum (P payload values per element), 2 top-k then softmax, 3 mean and variance.
+hipError_t launch_row_cascade(int kind, const float* x, const float* payload, int64_t R, int64_t N, int P, int k,
+                              float* out, int32_t* out_idx, hipStream_t stream);
+
 // Merge of per-segment partials into o [rows, D] (fp32 or bf16) and lse.
 hipError_t launch_segment_merge(const float* part_m, const float* part_s, const float* part_o,
                                 int64_t rows, int64_t nseg, int D, bool out_bf16, void* o,

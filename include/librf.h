@@ -216,6 +216,44 @@ RF_API rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, i
                                      int64_t d_qk, int64_t d_v, int64_t nseg, float scale, float* part_m,
                                      float* part_s, float* part_o, rf_stream stream);
 
+/* The cascades rf_row_cascade instantiates from one incremental template. */
+typedef enum rf_cascade {
+    RF_CASCADE_LOGSUMEXP = 0,        /* out[r] = m + ln sum_j exp(x_rj - m), m = max_j x_rj        */
+    RF_CASCADE_SOFTMAX_WEIGHTED = 1, /* out[r, :] = sum_j softmax(x_r)_j payload[r, j, :]         */
+    RF_CASCADE_TOPK_SOFTMAX = 2,     /* out[r, :] = softmax of the k best, out_idx[r, :] = indices */
+    RF_CASCADE_MEAN_VAR = 3          /* out[r, 0] = mean, out[r, 1] = population variance         */
+} rf_cascade;
+
+/*
+ * rf_row_cascade -- a cascaded reduction over each row of x, from a generic
+ * incremental template.
+ *
+ * The fusion conditions of the technical summary (Methodologie 1-2) and the
+ * explainer's sections 2.2-2.3 reduce any chain d_i = (+)_j G_i(x_j, d_<i) whose
+ * terms factor as H_i(d) G'_i(x) to one loop that keeps running values of every
+ * d_i and corrects them by H_i(d_new) H_i^-1(d_old) when an earlier d moves. The
+ * library's template takes such a cascade as (state, incremental update, merge of
+ * partial states) and folds each row with one wave; this entry point exposes four
+ * instances:
+ *   RF_CASCADE_LOGSUMEXP        max, then the sum of exp(x - max) (safe softmax's head);
+ *   RF_CASCADE_SOFTMAX_WEIGHTED max, sum of exp, then the exp-weighted sum of the payload
+ *                               (the attention chain with given scores);
+ *   RF_CASCADE_TOPK_SOFTMAX     the k best (score descending, index ascending), then the
+ *                               softmax over them (the MoE gate's tail, any k <= 8);
+ *   RF_CASCADE_MEAN_VAR         the mean, then the sum of squared deviations from it
+ *                               (Welford's update, Chan-Golub-LeVeque merge).
+ * Results are deterministic (fixed merge order); accumulation is fp32.
+ *
+ *   x        [R, N] fp32.   payload  [R, N, P] fp32 for RF_CASCADE_SOFTMAX_WEIGHTED, else NULL.
+ *   P        payload values per element: 1, 2, 4, 8 or 16 (softmax-weighted), else 0.
+ *   k        1 <= k <= min(8, N) for RF_CASCADE_TOPK_SOFTMAX, else ignored.
+ *   out      fp32: [R] (logsumexp), [R, P] (softmax-weighted), [R, k] (top-k weights),
+ *            [R, 2] (mean, variance).   out_idx  [R, k] int32 for top-k, else NULL.
+ *   Supported: R, N >= 1; R*N*max(P,1) below 2^40; N < 2^31.
+ */
+RF_API rf_status rf_row_cascade(rf_cascade kind, const float* x, const float* payload, int64_t R, int64_t N,
+                                int64_t P, int64_t k, float* out, int32_t* out_idx, rf_stream stream);
+
 /*
  * rf_moe_route_workspace_size -- bytes of device workspace rf_moe_route needs.
  */

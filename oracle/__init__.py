@@ -28,14 +28,15 @@ codec checks); no function is "parity unpinned".
 """
 from .attention import attention, attention_incremental, decode, decode_streaming, mla_decode
 from .segments import segment_bounds, split_partials, merge_partials, decode_split_merge
-from .moe import moe_route, gate_scores
+from .moe import moe_route, gate_scores, topk_softmax
+from . import cascade
 from .quant import (E4M3_MAX, e4m3fn_decode, e4m3fn_encode, fl32, quantize_rows,
                     quant_gemm, quant_gemm_acc)
 
 __all__ = [
     "attention", "attention_incremental", "decode", "decode_streaming", "mla_decode",
     "segment_bounds", "split_partials", "merge_partials", "decode_split_merge",
-    "moe_route", "gate_scores",
+    "moe_route", "gate_scores", "topk_softmax", "cascade",
     "E4M3_MAX", "e4m3fn_decode", "e4m3fn_encode", "fl32", "quantize_rows",
     "quant_gemm", "quant_gemm_acc",
 ]

@@ -19,9 +19,9 @@ def gate_scores(x, w_gate):
     return np.asarray(x, np.float64) @ np.asarray(w_gate, np.float64)
 
 
-def moe_route(x, w_gate, k: int):
-    """Returns (idx [T, k] int32, w [T, k] float64, scores [T, E] float64)."""
-    s = gate_scores(x, w_gate)
+def topk_softmax(s, k: int):
+    """The top-k -> softmax tail on given scores s [T, E]: returns (idx [T, k] int32, w [T, k])."""
+    s = np.asarray(s, np.float64)
     E = s.shape[1]
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
@@ -30,4 +30,11 @@ def moe_route(x, w_gate, k: int):
     top = np.take_along_axis(s, idx, axis=1)
     e = np.exp(top - top[:, :1])                    # top[:, 0] is the largest selected score
     w = e / e.sum(axis=1, keepdims=True)
-    return idx.astype(np.int32), w, s
+    return idx.astype(np.int32), w
+
+
+def moe_route(x, w_gate, k: int):
+    """Returns (idx [T, k] int32, w [T, k] float64, scores [T, E] float64)."""
+    s = gate_scores(x, w_gate)
+    idx, w = topk_softmax(s, k)
+    return idx, w, s

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
-        "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split",
+        "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split", "rf_row_cascade",
         "rf_moe_route_workspace_size",
         "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
@@ -201,3 +201,17 @@ def test_mla_validation(lib):
     assert call(scale=float("nan")) == INVALID
     assert call(po=P) == INVALID and b"alias" in lib.rf_last_error()       # part_o over q
     assert lib.rf_segment_merge(P, P2, P3, 4, 2, 256, 1, P4, None, None) == UNSUPPORTED   # D 256
+
+
+def test_row_cascade_validation(lib):
+    c = lib.rf_row_cascade
+    assert c(4, P, None, 2, 8, 0, 0, P2, None, None) == INVALID                 # unknown kind
+    assert c(0, None, None, 2, 8, 0, 0, P2, None, None) == INVALID              # x NULL
+    assert c(0, P, None, 0, 8, 0, 0, P2, None, None) == INVALID                 # R = 0
+    assert c(1, P, None, 2, 8, 4, 0, P2, None, None) == INVALID                 # payload NULL
+    assert c(1, P, P3, 2, 8, 3, 0, P2, None, None) == UNSUPPORTED               # P = 3
+    assert c(0, P, None, 2, 8, 2, 0, P2, None, None) == INVALID                 # P for logsumexp
+    assert c(2, P, None, 2, 8, 0, 9, P2, P3, None) == UNSUPPORTED               # k > 8
+    assert c(2, P, None, 2, 4, 0, 5, P2, P3, None) == UNSUPPORTED               # k > N
+    assert c(2, P, None, 2, 8, 0, 2, P2, None, None) == INVALID                 # out_idx NULL
+    assert c(3, P, None, 2, 8, 0, 0, P, None, None) == INVALID                  # out over x

@@ -1,0 +1,62 @@
+"""GPU parity: rf_row_cascade (the generic incremental template's instances) against the
+plain multi-pass definitions in oracle/cascade.py. fp32 inputs and fp32 accumulation:
+|g - r| <= 1e-5 + 1e-5 |r|; top-k indices bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cascade
+from tests.gpu_util import assert_close, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-5
+SHAPES = [(1, 1), (5, 3), (3, 255), (4, 256), (2, 257), (64, 1000), (7, 4096), (2, 4099)]
+
+
+def _x(R, N, seed, scale=3.0, shift=0.0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((R, N)) * scale + shift).astype(np.float32)
+
+
+@pytest.mark.parametrize("R,N", SHAPES)
+def test_logsumexp(rf, R, N):
+    x = _x(R, N, 10 + N)
+    got = host(rf.row_cascade("logsumexp", dev_f32(x)))
+    assert_close(got, cascade.logsumexp(x), ATOL, RTOL, "lse")
+
+
+@pytest.mark.parametrize("R,N", SHAPES)
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_softmax_weighted(rf, R, N, P):
+    x = _x(R, N, 20 + N + P)
+    p = np.random.default_rng(21 + N).standard_normal((R, N, P)).astype(np.float32)
+    got = host(rf.row_cascade("softmax_weighted", dev_f32(x), dev_f32(p)))
+    assert_close(got, cascade.softmax_weighted(x, p), ATOL, RTOL, "o")
+
+
+@pytest.mark.parametrize("R,N", [(5, 8), (3, 255), (64, 1000), (2, 4099)])
+@pytest.mark.parametrize("k", [1, 2, 5, 8])
+def test_topk_softmax(rf, R, N, k):
+    # Scores on a grid of 1/4: many exact ties, which must resolve to the lower index.
+    x = (np.round(_x(R, N, 30 + N + k) * 4) / 4).astype(np.float32)
+    w, idx = rf.row_cascade("topk_softmax", dev_f32(x), k=k)
+    ri, rw = oracle.topk_softmax(x.astype(np.float64), k)
+    np.testing.assert_array_equal(host(idx), ri)
+    assert_close(host(w), rw, ATOL, RTOL, "w")
+
+
+@pytest.mark.parametrize("R,N", SHAPES)
+def test_mean_var(rf, R, N):
+    x = _x(R, N, 40 + N, scale=3.0, shift=10.0)
+    got = host(rf.row_cascade("mean_var", dev_f32(x)))
+    assert_close(got, cascade.mean_var(x), ATOL, RTOL, "mean/var")
+
+
+def test_deterministic(rf):
+    x = dev_f32(_x(16, 5000, 50))
+    a = rf.row_cascade("mean_var", x)
+    b = rf.row_cascade("mean_var", x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
