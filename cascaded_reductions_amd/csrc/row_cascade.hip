@@ -1,8 +1,9 @@
 // Row cascades built from the generic incremental template (cascade.hpp).
 //
-// One wave folds one row of x [R, N] (fp32): lane l absorbs elements 4l .. 4l+3 of every
-// 256-element stretch (16-byte loads), then the 64 lane states are merged by xor shuffles
-// in a fixed order and lane 0 writes the row's result. The instances are the cascades
+// A group of G lanes folds one row of x [R, N] (fp32; G from 4 to 64 so that every lane
+// absorbs at least 32 elements): lane i absorbs elements 4i .. 4i+3 of every 4G-element
+// stretch (16-byte loads), then the group's states are merged by xor shuffles in a fixed
+// order and the group's first lane writes the row's result. The instances are the cascades
 // the technical summary "RedFuser: An Automatic Operator Fusion Framework for Cascaded
 // Reductions on AI Accelerators" (Methodologie 1-2) and the explainer
 // "RedFuser框架：AI加速器中的算子融合技术解析" (sections 2.2, 4.1, 4.2) use as examples,
@@ -19,57 +20,83 @@ namespace {
 
 using namespace cascade;
 
-template <class Spec>
+// G lanes fold one row (G in {4, 8, 16, 32, 64}; 64 / G rows per wave): lane i of the group
+// absorbs elements 4i .. 4i+3 of every 4G-element stretch (four 16-byte loads in flight
+// when there is no payload), then the group's states are merged by xor shuffles within
+// the group, in a fixed order.
+template <class Spec, int G>
 __device__ __forceinline__ typename Spec::State fold_row(const float* __restrict__ xr, const float* __restrict__ pr,
-                                                         int64_t N, int lane) {
+                                                         int64_t N, int li) {
     constexpr int P = Spec::kPayload;
+    constexpr int STRIDE = 4 * G;
     typename Spec::State st = Spec::identity();
-    const int64_t full = (N & 3) == 0 ? (N & ~int64_t(255)) : 0;   // 16-byte loads need aligned rows
-    for (int64_t j0 = 4 * lane; j0 < full; j0 += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + j0);
+    auto absorb4 = [&](const float4& v, int64_t j0) {
         const float xs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) Spec::absorb(st, xs[e], int32_t(j0 + e), P ? pr + (j0 + e) * P : nullptr);
-    }
-    for (int64_t j = full + lane; j < N; j += 64) Spec::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
+    };
+    const bool vec = (N & 3) == 0;            // 16-byte loads need aligned rows
+    // Four loads in flight when only x is read; with a payload its loads already overlap.
+    const int64_t full4 = vec && P == 0 ? N / (4 * STRIDE) * (4 * STRIDE) : 0;
+    int64_t j0 = 4 * li;
+    for (; j0 < full4; j0 += 4 * STRIDE) {
+        float4 v[4];
 #pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) st = Spec::combine(st, shfl_xor_state(st, mask));
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(xr + j0 + u * STRIDE);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) absorb4(v[u], j0 + u * STRIDE);
+    }
+    const int64_t full = vec ? N / STRIDE * STRIDE : 0;
+    for (; j0 < full; j0 += STRIDE) absorb4(*reinterpret_cast<const float4*>(xr + j0), j0);
+    for (int64_t j = full + li; j < N; j += G) Spec::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
+#pragma unroll
+    for (int mask = G / 2; mask >= 1; mask >>= 1) st = Spec::combine(st, shfl_xor_state(st, mask));
     return st;
 }
 
-__global__ __launch_bounds__(256) void lse_kernel(const float* __restrict__ x, int64_t R, int64_t N,
-                                                  float* __restrict__ out) {
-    const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (r >= R) return;
-    const auto st = fold_row<LogSumExp>(x + r * N, nullptr, N, lane);
-    if (lane == 0) out[r] = st.m + __logf(st.s);
+// Row r of this thread: 4 waves of 64 / G rows each per workgroup.
+template <int G>
+__device__ __forceinline__ int64_t row_of(int& li) {
+    li = int(threadIdx.x) & (G - 1);
+    return int64_t(blockIdx.x) * (256 / G) + (threadIdx.x / G);
 }
 
-template <int P>
+template <int G>
+__global__ __launch_bounds__(256) void lse_kernel(const float* __restrict__ x, int64_t R, int64_t N,
+                                                  float* __restrict__ out) {
+    int li;
+    const int64_t r = row_of<G>(li);
+    if (r >= R) return;
+    const auto st = fold_row<LogSumExp, G>(x + r * N, nullptr, N, li);
+    if (li == 0) out[r] = st.m + __logf(st.s);
+}
+
+template <int G, int P>
 __global__ __launch_bounds__(256) void softmax_weighted_kernel(const float* __restrict__ x,
                                                                const float* __restrict__ payload, int64_t R,
                                                                int64_t N, float* __restrict__ out) {
-    const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    int li;
+    const int64_t r = row_of<G>(li);
     if (r >= R) return;
-    const auto st = fold_row<SoftmaxWeighted<P>>(x + r * N, payload + r * N * P, N, lane);
-    if (lane < P) {
+    const auto st = fold_row<SoftmaxWeighted<P>, G>(x + r * N, payload + r * N * P, N, li);
+    for (int i0 = 0; i0 < P; i0 += G) {
+        const int i = i0 + li;
         float o = st.o[0];
 #pragma unroll
-        for (int i = 1; i < P; ++i) o = lane == i ? st.o[i] : o;
-        out[r * P + lane] = o / st.s;
+        for (int c = 1; c < P; ++c) o = i == c ? st.o[c] : o;
+        if (i < P) out[r * P + i] = o / st.s;
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ x, int64_t R, int64_t N, int k,
                                                            float* __restrict__ out, int32_t* __restrict__ out_idx) {
     constexpr int K = 8;
-    const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    int li;
+    const int64_t r = row_of<G>(li);
     if (r >= R) return;
-    const auto st = fold_row<TopK<K>>(x + r * N, nullptr, N, lane);
-    if (lane == 0) {
+    const auto st = fold_row<TopK<K>, G>(x + r * N, nullptr, N, li);
+    if (li == 0) {
         float e[K], den = 0.f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
@@ -86,42 +113,58 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(256) void mean_var_kernel(const float* __restrict__ x, int64_t R, int64_t N,
                                                        float* __restrict__ out) {
-    const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    int li;
+    const int64_t r = row_of<G>(li);
     if (r >= R) return;
-    const auto st = fold_row<MeanVar>(x + r * N, nullptr, N, lane);
-    if (lane == 0) {
+    const auto st = fold_row<MeanVar, G>(x + r * N, nullptr, N, li);
+    if (li == 0) {
         out[r * 2] = st.mean;
         out[r * 2 + 1] = st.m2 / st.n;
     }
+}
+
+template <int G>
+hipError_t launch_g(int kind, const float* x, const float* payload, int64_t R, int64_t N, int P, int k, float* out,
+                    int32_t* out_idx, hipStream_t stream) {
+    const int64_t blocks = ceil_div(R, int64_t(256 / G));
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid{unsigned(blocks), 1u, 1u}, block{256u, 1u, 1u};
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(lse_kernel<G>, grid, block, 0, stream, x, R, N, out); break;
+        case 1:
+            switch (P) {
+                case 1: hipLaunchKernelGGL((softmax_weighted_kernel<G, 1>), grid, block, 0, stream, x, payload, R, N, out); break;
+                case 2: hipLaunchKernelGGL((softmax_weighted_kernel<G, 2>), grid, block, 0, stream, x, payload, R, N, out); break;
+                case 4: hipLaunchKernelGGL((softmax_weighted_kernel<G, 4>), grid, block, 0, stream, x, payload, R, N, out); break;
+                case 8: hipLaunchKernelGGL((softmax_weighted_kernel<G, 8>), grid, block, 0, stream, x, payload, R, N, out); break;
+                case 16: hipLaunchKernelGGL((softmax_weighted_kernel<G, 16>), grid, block, 0, stream, x, payload, R, N, out); break;
+                default: return hipErrorInvalidValue;
+            }
+            break;
+        case 2: hipLaunchKernelGGL(topk_softmax_kernel<G>, grid, block, 0, stream, x, R, N, k, out, out_idx); break;
+        case 3: hipLaunchKernelGGL(mean_var_kernel<G>, grid, block, 0, stream, x, R, N, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_row_cascade(int kind, const float* x, const float* payload, int64_t R, int64_t N, int P, int k,
                               float* out, int32_t* out_idx, hipStream_t stream) {
-    const int64_t blocks = ceil_div(R, int64_t(4));
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    const dim3 grid{unsigned(blocks), 1u, 1u}, block{256u, 1u, 1u};
-    switch (kind) {
-        case 0: hipLaunchKernelGGL(lse_kernel, grid, block, 0, stream, x, R, N, out); break;
-        case 1:
-            switch (P) {
-                case 1: hipLaunchKernelGGL(softmax_weighted_kernel<1>, grid, block, 0, stream, x, payload, R, N, out); break;
-                case 2: hipLaunchKernelGGL(softmax_weighted_kernel<2>, grid, block, 0, stream, x, payload, R, N, out); break;
-                case 4: hipLaunchKernelGGL(softmax_weighted_kernel<4>, grid, block, 0, stream, x, payload, R, N, out); break;
-                case 8: hipLaunchKernelGGL(softmax_weighted_kernel<8>, grid, block, 0, stream, x, payload, R, N, out); break;
-                case 16: hipLaunchKernelGGL(softmax_weighted_kernel<16>, grid, block, 0, stream, x, payload, R, N, out); break;
-                default: return hipErrorInvalidValue;
-            }
-            break;
-        case 2: hipLaunchKernelGGL(topk_softmax_kernel, grid, block, 0, stream, x, R, N, k, out, out_idx); break;
-        case 3: hipLaunchKernelGGL(mean_var_kernel, grid, block, 0, stream, x, R, N, out); break;
-        default: return hipErrorInvalidValue;
+    // Lanes per row: enough that each lane absorbs at least 32 elements, at most a wave.
+    int64_t g = 4;
+    while (g < 64 && N >= 32 * 2 * g) g *= 2;
+    switch (g) {
+        case 4: return launch_g<4>(kind, x, payload, R, N, P, k, out, out_idx, stream);
+        case 8: return launch_g<8>(kind, x, payload, R, N, P, k, out, out_idx, stream);
+        case 16: return launch_g<16>(kind, x, payload, R, N, P, k, out, out_idx, stream);
+        case 32: return launch_g<32>(kind, x, payload, R, N, P, k, out, out_idx, stream);
+        default: return launch_g<64>(kind, x, payload, R, N, P, k, out, out_idx, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace rf
