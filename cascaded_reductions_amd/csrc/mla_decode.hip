@@ -78,12 +78,17 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     __shared__ __attribute__((aligned(16))) uint16_t ring[STAGES * TILE_ELEMS];
     __shared__ __attribute__((aligned(16))) float xbuf[NW][16][64];   // partial scores, [reg][lane]
 
-    // Workgroup -> (batch b, head block hb, segment t).
-    const int64_t bid = blockIdx.x;
-    const int64_t t = bid % nseg;
-    const int64_t rest = bid / nseg;
-    const int64_t hb = rest % nhb;
-    const int64_t b = rest / nhb;
+    // Workgroup -> (batch b, segment t, head block hb). Workgroups are dispatched round-robin
+    // over the 8 XCDs; renumbering gives each XCD a contiguous range of logical ids, and the
+    // head blocks of one (b, t) are consecutive ids, so they read the same cache tiles
+    // through one L2.
+    int64_t bid = blockIdx.x;
+    const int64_t total = int64_t(gridDim.x);
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int64_t hb = bid % nhb;
+    const int64_t rest = bid / nhb;
+    const int64_t t = rest % nseg;
+    const int64_t b = rest / nseg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
