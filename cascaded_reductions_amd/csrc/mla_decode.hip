@@ -170,12 +170,18 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         const uint16_t* tl = ring + slot * TILE_ELEMS;
 
         // Partial S^T = K Q^T over this half's 288 key values, then the partner's half.
-        f32x16 sc = f32x16{};
+        // Two accumulators (even and odd K-steps) halve the dependent MFMA chain; their sum
+        // is formed in a fixed order, so both halves of a pair still agree bit for bit. (Three
+        // measured slower.)
+        f32x16 sc0 = f32x16{}, sc1 = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NCQ; ++c) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + h));
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[c], sc, 0, 0, 0);
+        for (int c = 0; c < NCQ; c += 2) {
+            const u32x4 kf0 = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + h));
+            const u32x4 kf1 = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + 2 + h));
+            sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf0), qf[c], sc0, 0, 0, 0);
+            sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1), qf[c + 1], sc1, 0, 0, 0);
         }
+        f32x16 sc = sc0 + sc1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) xbuf[wave][r][lane] = sc[r];
         __syncthreads();
