@@ -76,7 +76,7 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       float* __restrict__ part_s, float* __restrict__ part_o) {
     constexpr int WLT = TILE_CHUNKS / 64 / NW;   // wave loads per tile and wave
     __shared__ __attribute__((aligned(16))) uint16_t ring[STAGES * TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) float xbuf[NW][16][64];   // partial scores, [reg][lane]
+    __shared__ __attribute__((aligned(16))) f32x4 xbuf[NW][4][64];    // partial scores, [reg/4][lane][4]
 
     // Workgroup -> (batch b, segment t, head block hb). Workgroups are dispatched round-robin
     // over the 8 XCDs; renumbering gives each XCD a contiguous range of logical ids, and the
@@ -183,10 +183,15 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
         f32x16 sc = sc0 + sc1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xbuf[wave][r][lane] = sc[r];
+        for (int q4 = 0; q4 < 4; ++q4)
+            xbuf[wave][q4][lane] = f32x4{sc[4 * q4], sc[4 * q4 + 1], sc[4 * q4 + 2], sc[4 * q4 + 3]};
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] += xbuf[wave ^ 1][r][lane];
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 o = xbuf[wave ^ 1][q4][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[4 * q4 + e] += o[e];
+        }
         const int64_t kleft = s1 - (s0 + int64_t(j) * KT);
         const int kvalid = kleft < KT ? int(kleft) : KT;
 #pragma unroll
