@@ -48,6 +48,8 @@ _SIGS = {
     "rf_attn_decode_split": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_segment_merge": ([_P, _P, _P, _I64, _I64, _I64, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
+    "rf_attn_decode_workspace_size": ([_I64, _I64, _I64, _I64, _I64], _SZ),
+    "rf_attn_decode": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _c.c_int, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_row_cascade": ([_c.c_int, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -202,15 +204,41 @@ def attn_decode_segments(rows: int, L: int, num_cus: int = 0) -> int:
     return n
 
 
-def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, out_dtype=None):
-    """Split + merge on the current stream: returns (o [B,H,D], lse [B,H]). With nseg None the
-    segment count comes from attn_decode_segments."""
+_dec_ws = {}
+
+
+def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, out_dtype=None, *, out=None,
+                lse=None):
+    """Decode attention in one call (rf_attn_decode): returns (o [B,H,D], lse [B,H]). nseg None
+    lets the library choose (one segment, a single launch, whenever the rows fill the chip)."""
+    torch = _torch()
     B, H, D = q.shape
-    if nseg is None:
-        nseg = attn_decode_segments(B * H, k.shape[2])
-    pm, ps, po = attn_decode_split(q, k, v, nseg, scale)
-    o, lse = segment_merge(pm, ps, po, out_dtype)
-    return o.view(B, H, D), lse.view(B, H)
+    L = k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, H, L, D))
+    _need(v, "v", torch.bfloat16, (B, H, L, D))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or torch.bfloat16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    n = 0 if nseg is None else int(nseg)
+    out = torch.empty((B, H, D), dtype=out_dtype, device=q.device) if out is None else out
+    _need(out, "out", out_dtype, (B, H, D))
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(lse, "lse", torch.float32, (B, H))
+    need = int(load().rf_attn_decode_workspace_size(B, H, L, D, n))
+    ws = None
+    if need:
+        key = (q.device.type, q.device.index)
+        ws = _dec_ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _dec_ws[key] = ws
+    _check(load().rf_attn_decode(_ptr(q), _ptr(k), _ptr(v), B, H, L, D, n, float(scale),
+                                 RF_F32 if out_dtype == torch.float32 else RF_BF16, _ptr(out), _ptr(lse), _ptr(ws),
+                                 need, _stream(q)))
+    return out, lse
 
 
 # ------------------------------------------------------------------ MLA decode

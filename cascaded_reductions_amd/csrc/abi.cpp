@@ -190,6 +190,75 @@ rf_status rf_attn_decode_split(const void* q, const void* k, const void* v, int6
     return device_status(e, "rf_attn_decode_split launch");
 }
 
+namespace {
+// Partials of rf_attn_decode: part_m, part_s [rows * nseg] and part_o [rows * nseg * D] fp32,
+// each section starting on a 256-byte boundary.
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t decode_ws_bytes(int64_t rows, int64_t D, int64_t nseg) {
+    if (nseg <= 1) return 0;
+    const size_t n = size_t(rows) * size_t(nseg);
+    return 2 * round256(n * 4) + round256(n * size_t(D) * 4);
+}
+}  // namespace
+
+size_t rf_attn_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t D, int64_t nseg) {
+    int64_t rows;
+    if (B < 1 || H < 1 || L < 1 || (D != 64 && D != 128) || nseg < 0 || !prod({B, H}, &rows)) return 0;
+    if (nseg == 0) nseg = rf_attn_decode_segments(rows, L, 0);
+    if (nseg > L || nseg > 1024) return 0;
+    return decode_ws_bytes(rows, D, nseg);
+}
+
+rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L, int64_t D,
+                         int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse, void* workspace,
+                         size_t ws_bytes, rf_stream stream) {
+    RF_PTR(q, "q");
+    RF_PTR(k, "k");
+    RF_PTR(v, "v");
+    RF_PTR(o, "o");
+    RF_OPT_PTR(lse, "lse");
+    RF_REQUIRE(out_dt == RF_F32 || out_dt == RF_BF16, RF_ERR_INVALID_ARGUMENT, "out_dt must be RF_F32 or RF_BF16");
+    RF_REQUIRE(B >= 1 && H >= 1 && L >= 1, RF_ERR_INVALID_ARGUMENT, "B, H and L must be >= 1");
+    RF_REQUIRE(D == 64 || D == 128, RF_ERR_UNSUPPORTED, "D must be 64 or 128 (got %lld)", (long long)D);
+    RF_REQUIRE(nseg >= 0 && nseg <= L && nseg <= 1024, RF_ERR_INVALID_ARGUMENT,
+               "nseg must be in [0, min(L, 1024)] (got %lld)", (long long)nseg);
+    RF_REQUIRE(scale == scale && scale - scale == 0.0f, RF_ERR_INVALID_ARGUMENT, "scale must be finite");
+    int64_t rows, nkv, nq;
+    RF_REQUIRE(prod({B, H}, &rows) && prod({rows, L, D}, &nkv) && nkv < kMaxElems && prod({rows, D}, &nq) &&
+                   rows <= INT32_MAX,
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    if (nseg == 0) nseg = rf_attn_decode_segments(rows, L, 0);
+    const uint64_t oes = out_dt == RF_F32 ? 4 : 2;
+    RF_REQUIRE(!overlap(o, nq * oes, q, nq * 2) && !overlap(o, nq * oes, k, nkv * 2) &&
+                   !overlap(o, nq * oes, v, nkv * 2) && !overlap(lse, rows * 4, q, nq * 2) &&
+                   !overlap(lse, rows * 4, k, nkv * 2) && !overlap(lse, rows * 4, v, nkv * 2) &&
+                   !overlap(lse, rows * 4, o, nq * oes),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nseg == 1) {
+        const hipError_t e = rf::launch_decode_direct(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                                      static_cast<const uint16_t*>(v), rows, L, int(D), scale,
+                                                      out_dt == RF_BF16, o, lse, s);
+        return device_status(e, "rf_attn_decode launch");
+    }
+    const size_t need = decode_ws_bytes(rows, D, nseg);
+    RF_REQUIRE(ws_bytes >= need, RF_ERR_BUFFER_TOO_SMALL, "workspace too small: %zu bytes, need %zu", ws_bytes, need);
+    RF_PTR(workspace, "workspace");
+    const uint64_t n = uint64_t(rows) * uint64_t(nseg);
+    RF_REQUIRE(!overlap(workspace, need, q, nq * 2) && !overlap(workspace, need, k, nkv * 2) &&
+                   !overlap(workspace, need, v, nkv * 2) && !overlap(workspace, need, o, nq * oes) &&
+                   !overlap(workspace, need, lse, rows * 4),
+               RF_ERR_INVALID_ARGUMENT, "workspace must not alias the tensors");
+    float* pm = static_cast<float*>(workspace);
+    float* ps = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(n * 4));
+    float* po = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * round256(n * 4));
+    hipError_t e = rf::launch_decode_split(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), rows, L, int(D), nseg, scale, pm, ps, po,
+                                           s);
+    if (e == hipSuccess) e = rf::launch_segment_merge(pm, ps, po, rows, nseg, int(D), out_dt == RF_BF16, o, lse, s);
+    return device_status(e, "rf_attn_decode launch");
+}
+
 rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t H, int64_t L, int64_t d_qk,
                               int64_t d_v, int64_t nseg, float scale, float* part_m, float* part_s,
                               float* part_o, rf_stream stream) {

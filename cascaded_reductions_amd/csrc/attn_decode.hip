@@ -21,14 +21,18 @@
 namespace rf {
 namespace {
 
-template <int D, int U>
+// DIRECT: a single segment per row (the Single-Segment strategy for decode): the wave
+// normalises its own state and writes o (bf16 or fp32) and lse; no partials, no merge.
+template <int D, int U, bool DIRECT = false>
 __global__ __launch_bounds__(64) void decode_split_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           int64_t L, int64_t nseg, int64_t seglen,
                                                           float scale_log2, float* __restrict__ part_m,
                                                           float* __restrict__ part_s,
-                                                          float* __restrict__ part_o) {
+                                                          float* __restrict__ part_o,
+                                                          void* __restrict__ out = nullptr, int out_bf16 = 0,
+                                                          float* __restrict__ lse = nullptr) {
     constexpr int LPK = D / 8;      // lanes per key row
     constexpr int KPW = 64 / LPK;   // key slots per wave load
     const int64_t wid = blockIdx.x; // row * nseg + segment
@@ -114,7 +118,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const uint16_t* __rest
             m = M;
         }
     }
-    if (slot == 0) {
+    if constexpr (DIRECT) {
+        if (slot == 0) {                      // L >= 1, so the single segment is never empty
+            const float inv = 1.f / s;
+            if (out_bf16) {
+                uint4 w;
+                w.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+                w.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+                w.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+                w.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r * D + c * 8) = w;
+            } else {
+                float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + r * D + c * 8);
+                dst[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+                dst[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+            }
+            if (lse && c == 0) lse[r] = m * kLn2 + __logf(s);
+        }
+    } else if (slot == 0) {
         float4* dst = reinterpret_cast<float4*>(part_o + wid * D + c * 8);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
@@ -208,6 +229,19 @@ hipError_t launch_decode_split(const uint16_t* q, const uint16_t* k, const uint1
     else
         hipLaunchKernelGGL((decode_split_kernel<64, 4>), dim3(unsigned(blocks)), dim3(64), 0, stream, q, k, v, L,
                            nseg, seglen, sl2, part_m, part_s, part_o);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_direct(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t R, int64_t L, int D,
+                                float scale, bool out_bf16, void* o, float* lse, hipStream_t stream) {
+    if (R > INT32_MAX) return hipErrorInvalidValue;
+    const float sl2 = scale * kLog2e;
+    if (D == 128)
+        hipLaunchKernelGGL((decode_split_kernel<128, 4, true>), dim3(unsigned(R)), dim3(64), 0, stream, q, k, v, L,
+                           int64_t(1), L, sl2, nullptr, nullptr, nullptr, o, int(out_bf16), lse);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<64, 4, true>), dim3(unsigned(R)), dim3(64), 0, stream, q, k, v, L,
+                           int64_t(1), L, sl2, nullptr, nullptr, nullptr, o, int(out_bf16), lse);
     return hipGetLastError();
 }
 

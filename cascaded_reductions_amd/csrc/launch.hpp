@@ -37,6 +37,10 @@ hipError_t launch_mla_decode_split(const uint16_t* q, const uint16_t* kv, int64_
 hipError_t launch_row_cascade(int kind, const float* x, const float* payload, int64_t R, int64_t N, int P, int k,
                               float* out, int32_t* out_idx, hipStream_t stream);
 
+// Single-segment decode: each wave reduces a whole row and writes o [R, D] (bf16 or fp32) and lse.
+hipError_t launch_decode_direct(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t R, int64_t L, int D,
+                                float scale, bool out_bf16, void* o, float* lse, hipStream_t stream);
+
 // Merge of per-segment partials into o [rows, D] (fp32 or bf16) and lse.
 hipError_t launch_segment_merge(const float* part_m, const float* part_s, const float* part_o,
                                 int64_t rows, int64_t nseg, int D, bool out_bf16, void* o,

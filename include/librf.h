@@ -189,6 +189,31 @@ RF_API rf_status rf_segment_merge(const float* part_m, const float* part_s, cons
                            float* lse, rf_stream stream);
 
 /*
+ * rf_attn_decode_workspace_size -- bytes of device workspace rf_attn_decode needs for the
+ * partials of nseg segments (nseg = 0: the rf_attn_decode_segments choice on the current
+ * device); 0 when one segment is used. Returns 0 for invalid sizes as well.
+ */
+RF_API size_t rf_attn_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t D, int64_t nseg);
+
+/*
+ * rf_attn_decode -- decode attention in one call: o = softmax(scale * q K^T) V per (b, h).
+ *
+ * With one segment (the Single-Segment strategy of the technical summary,
+ * Methodologie 3) each row is reduced by one wave in the incremental form and
+ * normalised in place: one launch, no partials. With nseg > 1 it runs
+ * rf_attn_decode_split into `workspace` and then rf_segment_merge (the
+ * Multi-Segment strategy). nseg = 0 asks rf_attn_decode_segments, which picks one
+ * segment whenever the rows alone give every SIMD a wave.
+ *
+ *   q [B, H, D], k, v [B, H, L, D] bf16.   out_dt RF_F32 or RF_BF16: o [B, H, D].
+ *   lse [B, H] fp32 or NULL.   workspace: rf_attn_decode_workspace_size bytes (NULL if 0).
+ *   Supported: as rf_attn_decode_split; 0 <= nseg <= min(L, 1024).
+ */
+RF_API rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L,
+                                int64_t D, int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse,
+                                void* workspace, size_t ws_bytes, rf_stream stream);
+
+/*
  * rf_mla_decode_split -- multi-head latent attention (MLA) decode, first kernel of two.
  *
  * MLA (named among the workloads of the technical summary's "Resultaten") caches

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
         "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split", "rf_row_cascade",
+        "rf_attn_decode_workspace_size", "rf_attn_decode",
         "rf_moe_route_workspace_size",
         "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
@@ -215,3 +216,21 @@ def test_row_cascade_validation(lib):
     assert c(2, P, None, 2, 4, 0, 5, P2, P3, None) == UNSUPPORTED               # k > N
     assert c(2, P, None, 2, 8, 0, 2, P2, None, None) == INVALID                 # out_idx NULL
     assert c(3, P, None, 2, 8, 0, 0, P, None, None) == INVALID                  # out over x
+
+
+def test_decode_one_call_validation(lib):
+    ws = lib.rf_attn_decode_workspace_size
+    assert ws(32, 32, 2048, 128, 1) == 0                      # one segment: no partials
+    assert ws(2, 4, 300, 128, 3) == 2 * 256 + (8 * 3 * 128 * 4 + 255) // 256 * 256
+    assert ws(2, 4, 300, 96, 3) == 0 and ws(2, 4, 300, 128, 301) == 0
+    d = lib.rf_attn_decode
+
+    def call(nseg=3, ws_bytes=0, wsp=None, o=P4, D=128, L=300):
+        return d(P, P2, P3, 2, 4, L, D, nseg, 0.08, 1, o, None, wsp, ws_bytes, None)
+    assert call(ws_bytes=16) == TOO_SMALL and b"workspace" in lib.rf_last_error()
+    assert call(nseg=301) == INVALID
+    assert call(nseg=-1) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    assert call(o=P) == INVALID                               # o over q
+    need = ws(2, 4, 300, 128, 3)
+    assert call(ws_bytes=need, wsp=P4) == INVALID             # workspace over o

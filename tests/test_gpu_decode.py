@@ -146,3 +146,21 @@ def test_decode_l16384_sampled(rf, nseg):
             heads, scale):
         assert_close(go[b, h], ro, ATOL, RTOL, f"O[{b},{h}]")
         assert_close(gl[b, h], rl, ATOL, RTOL, f"lse[{b},{h}]")
+
+
+@pytest.mark.parametrize("B,H,L,D,nseg", [
+    (2, 4, 300, 128, 1),      # one segment: a single launch writes o and lse
+    (1, 3, 1, 64, 1),         # one key
+    (2, 2, 517, 64, 1),
+    (2, 4, 300, 128, 3),      # split + merge through the workspace
+    (4, 8, 1000, 128, 0),     # automatic count
+])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_one_call_decode(rf, B, H, L, D, nseg, out_dtype):
+    q, k, v, scale = decode_inputs(B, H, L, D, seed=70 + L + nseg)
+    o, lse = rf.attn_decode(dev_bf16(q), dev_bf16(k), dev_bf16(v), nseg or None, scale, out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(_f(q), _f(k), _f(v), scale)
+    atol, rtol = (ATOL, RTOL) if out_dtype == torch.bfloat16 else (1e-3, 1e-3)
+    assert_close(host(o), ro, atol, rtol, "O")
+    assert_close(host(lse), rl, ATOL, RTOL, "lse")
