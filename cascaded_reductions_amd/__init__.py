@@ -204,7 +204,19 @@ def attn_decode_segments(rows: int, L: int, num_cus: int = 0) -> int:
     return n
 
 
-_dec_ws = {}
+_ws_cache = {}
+
+
+def _workspace(tag, device, nbytes):
+    """A scratch buffer per (entry point, device, current stream), grown on demand. Calls on
+    one stream are ordered, so they can share it; another stream gets its own buffer."""
+    torch = _torch()
+    key = (tag, device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
 
 
 def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, out_dtype=None, *, out=None,
@@ -228,13 +240,7 @@ def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, ou
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
     _need(lse, "lse", torch.float32, (B, H))
     need = int(load().rf_attn_decode_workspace_size(B, H, L, D, n))
-    ws = None
-    if need:
-        key = (q.device.type, q.device.index)
-        ws = _dec_ws.get(key)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-            _dec_ws[key] = ws
+    ws = _workspace("decode", q.device, need) if need else None
     _check(load().rf_attn_decode(_ptr(q), _ptr(k), _ptr(v), B, H, L, D, n, float(scale),
                                  RF_F32 if out_dtype == torch.float32 else RF_BF16, _ptr(out), _ptr(lse), _ptr(ws),
                                  need, _stream(q)))
@@ -310,19 +316,8 @@ def moe_route_workspace_size(T: int, Hd: int, E: int) -> int:
     return int(load().rf_moe_route_workspace_size(T, Hd, E))
 
 
-_moe_ws = {}
-
-
 def _moe_workspace(device, nbytes):
-    """A workspace per device, grown on demand; calls that share it must be ordered
-    (same stream), as with any scratch buffer."""
-    torch = _torch()
-    key = (device.type, device.index)
-    ws = _moe_ws.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-        _moe_ws[key] = ws
-    return ws
+    return _workspace("moe", device, nbytes)
 
 
 def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False, workspace=None):
