@@ -15,7 +15,7 @@
 // Because the heads share the cache row, the per-token work is a small GEMM
 // and runs on the matrix cores: a workgroup owns one batch entry, 64 heads and
 // one key segment, and walks the segment in tiles of 32 tokens staged in LDS (a
-// 3-slot ring filled by direct global-to-LDS loads two tiles ahead). Its four
+// 4-slot ring filled by direct global-to-LDS loads three tiles ahead). Its four
 // waves are two head blocks of 32 x two halves: half e of a head block forms the
 // scores over key values [288 e, 288 e + 288) and the output over latent values
 // [256 e, 256 e + 256), so a wave holds half of Q (72 registers) and half of the
@@ -53,7 +53,7 @@ constexpr int TILE_CHUNKS = KT * RCH;    // 2304
 constexpr int TILE_ELEMS = KT * DQK;     // 18432 bf16 = 36 KiB
 constexpr int NCQ = DQK / 32;            // K=16 steps of one half's partial scores (18)
 constexpr int DBV = DV / 64;             // 32-wide latent blocks of one half's output (8)
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;                // ring slots: 4 x 36 KiB + 16 KiB of score exchange = 160 KiB
 constexpr int NW = 4;                    // waves: 2 head blocks x 2 halves
 constexpr int HPW = 64;                  // heads per workgroup
 
@@ -64,6 +64,29 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 __device__ __forceinline__ bf16x4_t read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+}
+
+// O^T += V^T P^T on an accumulator kept in AGPRs (the matrix instruction reads and writes
+// them directly; the compiler would otherwise copy the 128 accumulator registers of a
+// wave between AGPRs and VGPRs on every tile). As inline assembly the instruction is
+// outside the compiler's hazard tracking, so the required wait states are explicit:
+// FIRST puts 5 before the instruction, covering a vector ALU write of the P operand (or
+// of the accumulator, by a rescale) just before it; accumulator chains on the same
+// registers need none; reads of the accumulator after the last one wait in agpr_settle.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FIRST)
+        asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// 24 wait states before any other instruction touches the accumulators written by mfma_pv
+// (more than the 18 a 16-pass matrix instruction needs before a vector read).
+__device__ __forceinline__ void agpr_settle(f32x16 (&acc)[8]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
+                   "+a"(acc[6]), "+a"(acc[7]));
 }
 
 // Element offset of logical 8-element chunk c of token row r inside a tile: the chunk
@@ -101,20 +124,35 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const uint16_t* kvb = kv + b * L * DQK;
 
     // Tile j of the segment into ring slot `slot`: wave load i (i = wave + NW * w) covers
-    // physical chunks [64 i, 64 i + 64) of the tile; tokens past the segment re-read its
-    // last token (their scores are masked).
+    // physical chunks [64 i, 64 i + 64) of the tile, so lane `lane` lands in token row
+    // r = (64 i + lane) / RCH at physical chunk pc and fetches the logical chunk pc ^ (r & 7)
+    // that the read side expects there. The byte offsets inside a tile do not depend on
+    // the tile and are formed once; a tile that runs past the segment re-reads its last
+    // token for the rows beyond it (their scores are masked).
+    uint32_t goff[WLT];
+#pragma unroll
+    for (int w = 0; w < WLT; ++w) {
+        const int p = (wave + NW * w) * 64 + lane;
+        const int r = p / RCH;
+        const int lc = (p - r * RCH) ^ (r & 7);
+        goff[w] = uint32_t(r * DQK + lc * 8) * 2u;
+    }
+    const uint32_t ring_lds = lds_addr(ring);
     auto issue = [&](int j, int slot) {
         const int64_t k0 = s0 + int64_t(j) * KT;
+        const uint16_t* gbase = kvb + k0 * DQK;                       // wave-uniform
+        const uint32_t lbase = ring_lds + uint32_t(slot * TILE_ELEMS * 2);
+        if (k0 + KT <= s1) {
 #pragma unroll
-        for (int w = 0; w < WLT; ++w) {
-            const int i = wave + NW * w;
-            const int p = i * 64 + lane;
-            const int r = p / RCH;
-            const int pc = p - r * RCH;
-            const int lc = pc ^ (r & 7);
-            int64_t key = k0 + r;
-            key = key < s1 ? key : s1 - 1;
-            lds_dma16(kvb + key * DQK + lc * 8, ring + slot * TILE_ELEMS + i * 512);
+            for (int w = 0; w < WLT; ++w) lds_dma16_sb(gbase, goff[w], lbase + uint32_t((wave + NW * w) * 1024));
+        } else {
+            const int rmax = int(s1 - 1 - k0);
+#pragma unroll
+            for (int w = 0; w < WLT; ++w) {
+                const int r = ((wave + NW * w) * 64 + lane) / RCH;
+                const int dr = r > rmax ? r - rmax : 0;              // rows past the end move back
+                lds_dma16_sb(gbase, goff[w] - uint32_t(dr * DQK * 2), lbase + uint32_t((wave + NW * w) * 1024));
+            }
         }
     };
 
@@ -139,17 +177,14 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     float m_ref = kNegInf, s_part = 0.f;
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 
-    // p = 2^(x sl2 - ref) for the 16 scores of the lane, packed to bf16; masked tokens
-    // (at or past kvalid) get 0. Returns the lane's sum of the packed values.
-    auto probs = [&](const f32x16& sc, int kvalid, uint32_t (&pk)[8]) {
+    // p = 2^(x sl2 - ref) for the 16 scores of the lane, packed to bf16. Returns the lane's
+    // sum of the packed values.
+    auto probs = [&](const f32x16& sc, uint32_t (&pk)[8]) {
         float t0 = 0.f, t1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            float p0 = exp2_fast(fmaf(sc[r], sl2, -m_ref));
-            float p1 = exp2_fast(fmaf(sc[r + 1], sl2, -m_ref));
-            const int key = (r >> 2) * 8 + 4 * h + (r & 3);
-            p0 = key < kvalid ? p0 : 0.f;
-            p1 = key + 1 < kvalid ? p1 : 0.f;
+            const float p0 = exp2_fast(fmaf(sc[r], sl2, -m_ref));
+            const float p1 = exp2_fast(fmaf(sc[r + 1], sl2, -m_ref));
             const uint32_t w = pack2(p0, p1);
             pk[r >> 1] = w;
             if (r & 2) t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, t1, false);
@@ -157,27 +192,46 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         }
         return t0 + t1;
     };
+    // Tail tiles: zero the probabilities of tokens at or past kvalid and return the new sum.
+    // (Rows past the segment hold copies of its last token, so their scores are finite and
+    // never exceed the valid maximum; only their weights must go.)
+    auto mask_tail = [&](int kvalid, uint32_t (&pk)[8]) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = (i >> 1) * 8 + 4 * h + 2 * (i & 1);
+            const uint32_t keep = (key < kvalid ? 0x0000FFFFu : 0u) | (key + 1 < kvalid ? 0xFFFF0000u : 0u);
+            pk[i] &= keep;
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, t, false);
+        }
+        return t;
+    };
 
+    // Read-side LDS element offsets inside a tile, formed once. The swizzle only touches
+    // the low three bits of a chunk index, so chunks 8 apart (and rows 8 apart) stay a
+    // constant distance apart and every other read is an immediate offset from these.
     const int j16 = lane & 15;
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
-    for (int j = 0; j < ntiles; ++j) {
-        const int slot = j % STAGES;
-        if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");   // tile j is in
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                       // every wave's part of tile j; tile j - 1 retired
-        if (j + 2 < ntiles) issue(j + 2, (j + 2) % STAGES);
-        const uint16_t* tl = ring + slot * TILE_ELEMS;
+    int kbase[4];                            // S: row l32, chunk 36 half + 2 cc + h (+8 per 4 K-steps)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) kbase[cc] = tile_off(l32, 36 * half + 2 * cc + h);
+    int vbase[2];                            // PV: token 4h + j/4, latent 256 half + 32 e + ...
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int col = 256 * half + 32 * e + 16 * (l32 >> 4) + 4 * (j16 & 3);
+        const int key0 = 4 * h + (j16 >> 2);
+        vbase[e] = tile_off(key0, col >> 3) + (col & 7);
+    }
 
+    // One tile; kvalid < KT only on the segment's last tile.
+    auto tile = [&](const uint16_t* tl, int kvalid) {
         // Partial S^T = K Q^T over this half's 288 key values, then the partner's half.
         // Two accumulators (even and odd K-steps) halve the dependent MFMA chain; their sum
-        // is formed in a fixed order, so both halves of a pair still agree bit for bit. (Three
-        // measured slower.)
+        // is formed in a fixed order, so both halves of a pair still agree bit for bit.
         f32x16 sc0 = f32x16{}, sc1 = f32x16{};
 #pragma unroll
         for (int c = 0; c < NCQ; c += 2) {
-            const u32x4 kf0 = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + h));
-            const u32x4 kf1 = *reinterpret_cast<const u32x4*>(tl + tile_off(l32, 36 * half + 2 * c + 2 + h));
+            const u32x4 kf0 = *reinterpret_cast<const u32x4*>(tl + kbase[c & 3] + (c >> 2) * 64);
+            const u32x4 kf1 = *reinterpret_cast<const u32x4*>(tl + kbase[(c + 1) & 3] + ((c + 1) >> 2) * 64);
             sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf0), qf[c], sc0, 0, 0, 0);
             sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1), qf[c + 1], sc1, 0, 0, 0);
         }
@@ -192,16 +246,10 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
             for (int e = 0; e < 4; ++e) sc[4 * q4 + e] += o[e];
         }
-        const int64_t kleft = s1 - (s0 + int64_t(j) * KT);
-        const int kvalid = kleft < KT ? int(kleft) : KT;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = (r >> 2) * 8 + 4 * h + (r & 3);
-            if (key >= kvalid) sc[r] = kNegInf;
-        }
 
         uint32_t pk[8];
-        float tsum = probs(sc, kvalid, pk);
+        float tsum = probs(sc, pk);
+        if (kvalid < KT) tsum = mask_tail(kvalid, pk);
         if (__any(!(tsum <= 256.f))) {         // exact path: row maximum, maybe a new reference
             float mx = kNegInf;
 #pragma unroll
@@ -210,34 +258,50 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             const float mx2 = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
             if (mx2 > m_ref) {
                 const float alpha = exp2_fast(m_ref - mx2);   // 0 on the first tile
+                agpr_settle(acc_o);
                 s_part *= alpha;
 #pragma unroll
                 for (int d = 0; d < DBV; ++d) acc_o[d] *= alpha;
                 m_ref = mx2;
             }
-            tsum = probs(sc, kvalid, pk);
+            tsum = probs(sc, pk);
+            if (kvalid < KT) tsum = mask_tail(kvalid, pk);
         }
         s_part += tsum;
 
-        // O^T += V^T P^T over the tile's two 16-token chunks.
+        // O^T += V^T P^T over the tile's two 16-token chunks; block d of 32 latent values
+        // reads tokens key0 and key0 + 8 (16-lane group layout of the transposing read).
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             const u32x4 pb = {pk[kc * 4 + 0], pk[kc * 4 + 1], pk[kc * 4 + 2], pk[kc * 4 + 3]};
-            const int key0 = kc * 16 + 4 * h + (j16 >> 2);
-            const int key1 = key0 + 8;
 #pragma unroll
             for (int d = 0; d < DBV; ++d) {
-                // 16-lane group: tokens key0 (key1), latent columns 256 half + 32d + 16 (l32/16) + 4 (j%4) .. +3.
-                const int col = 256 * half + 32 * d + 16 * (l32 >> 4) + 4 * (j16 & 3);
-                const bf16x4_t lo = read_tr16(tl + tile_off(key0, col >> 3) + (col & 7));
-                const bf16x4_t hi = read_tr16(tl + tile_off(key1, col >> 3) + (col & 7));
+                const uint16_t* vp = tl + vbase[d & 1] + kc * 16 * DQK + (d >> 1) * 64;
+                const bf16x4_t lo = read_tr16(vp);
+                const bf16x4_t hi = read_tr16(vp + 8 * DQK);
                 const bf16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
-                                                                    __builtin_bit_cast(bf16x8, pb), acc_o[d], 0, 0, 0);
+                if (d == 0) mfma_pv<true>(acc_o[d], __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb));
+                else mfma_pv<false>(acc_o[d], __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb));
             }
         }
+    };
+
+    if (ntiles > 0) issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+    if (ntiles > 2) issue(2, 2);
+    for (int j = 0; j < ntiles; ++j) {
+        const int slot = j % STAGES;
+        if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WLT) : "memory");   // tile j is in
+        else if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                       // every wave's part of tile j; tile j - 1 retired
+        if (j + 3 < ntiles) issue(j + 3, (j + 3) % STAGES);
+        const uint16_t* tl = ring + slot * TILE_ELEMS;
+        const int64_t kleft = s1 - (s0 + int64_t(j) * KT);
+        tile(tl, kleft < KT ? int(kleft) : KT);
     }
 
+    agpr_settle(acc_o);
     // Partials of (row = b * H + head, segment t); both halves hold the same m and s.
     const float s_row = s_part + __shfl_xor(s_part, 32, 64);
     if (head < H) {
