@@ -30,6 +30,9 @@
 //   * the reference maximum is lazy, as in the prefill kernel: a lane whose tile
 //     probabilities sum to at most 2^8 needs no rescale; otherwise the exact row
 //     maximum moves the reference (first tile included).
+// The tiles are software-pipelined: the score MFMAs of tile j + 1 are issued while
+// the vector ALUs form tile j's probabilities, and tile j's PV MFMAs run while the
+// halves swap tile j + 1's partial scores. The output accumulators stay in AGPRs.
 // Partials: part_m holds each segment's reference in natural units, part_s and
 // part_o the sum and the unnormalised accumulator relative to it -- the same
 // triple the merge combines exactly whatever the reference is.
@@ -222,11 +225,10 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         vbase[e] = tile_off(key0, col >> 3) + (col & 7);
     }
 
-    // One tile; kvalid < KT only on the segment's last tile.
-    auto tile = [&](const uint16_t* tl, int kvalid) {
-        // Partial S^T = K Q^T over this half's 288 key values, then the partner's half.
-        // Two accumulators (even and odd K-steps) halve the dependent MFMA chain; their sum
-        // is formed in a fixed order, so both halves of a pair still agree bit for bit.
+    // Partial S^T = K Q^T of one tile over this half's 288 key values. Two accumulators (even
+    // and odd K-steps) halve the dependent MFMA chain; their sum is formed in a fixed order,
+    // so both halves of a pair agree bit for bit once the partner's part is added.
+    auto scores = [&](const uint16_t* tl) {
         f32x16 sc0 = f32x16{}, sc1 = f32x16{};
 #pragma unroll
         for (int c = 0; c < NCQ; c += 2) {
@@ -235,7 +237,10 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf0), qf[c], sc0, 0, 0, 0);
             sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1), qf[c + 1], sc1, 0, 0, 0);
         }
-        f32x16 sc = sc0 + sc1;
+        return sc0 + sc1;
+    };
+    // The two halves of a head block swap partial scores through LDS (one barrier).
+    auto exchange = [&](f32x16 sc) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             xbuf[wave][q4][lane] = f32x4{sc[4 * q4], sc[4 * q4 + 1], sc[4 * q4 + 2], sc[4 * q4 + 3]};
@@ -246,11 +251,14 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
             for (int e = 0; e < 4; ++e) sc[4 * q4 + e] += o[e];
         }
-
-        uint32_t pk[8];
+        return sc;
+    };
+    // Probabilities of one tile's full scores (lazy reference; the exact path when a lane's
+    // sum exceeds 2^8), accumulated into s_part.
+    auto softmax = [&](const f32x16& sc, int kvalid, uint32_t (&pk)[8]) {
         float tsum = probs(sc, pk);
         if (kvalid < KT) tsum = mask_tail(kvalid, pk);
-        if (__any(!(tsum <= 256.f))) {         // exact path: row maximum, maybe a new reference
+        if (__any(!(tsum <= 256.f))) {
             float mx = kNegInf;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
@@ -268,9 +276,10 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             if (kvalid < KT) tsum = mask_tail(kvalid, pk);
         }
         s_part += tsum;
-
-        // O^T += V^T P^T over the tile's two 16-token chunks; block d of 32 latent values
-        // reads tokens key0 and key0 + 8 (16-lane group layout of the transposing read).
+    };
+    // O^T += V^T P^T over the tile's two 16-token chunks; block d of 32 latent values
+    // reads tokens key0 and key0 + 8 (16-lane group layout of the transposing read).
+    auto pv = [&](const uint16_t* tl, const uint32_t (&pk)[8]) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             const u32x4 pb = {pk[kc * 4 + 0], pk[kc * 4 + 1], pk[kc * 4 + 2], pk[kc * 4 + 3]};
@@ -285,20 +294,41 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             }
         }
     };
-
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
-    if (ntiles > 2) issue(2, 2);
-    for (int j = 0; j < ntiles; ++j) {
-        const int slot = j % STAGES;
-        if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WLT) : "memory");   // tile j is in
-        else if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                       // every wave's part of tile j; tile j - 1 retired
-        if (j + 3 < ntiles) issue(j + 3, (j + 3) % STAGES);
-        const uint16_t* tl = ring + slot * TILE_ELEMS;
+    auto kvalid_of = [&](int j) {
         const int64_t kleft = s1 - (s0 + int64_t(j) * KT);
-        tile(tl, kleft < KT ? int(kleft) : KT);
+        return kleft < KT ? int(kleft) : KT;
+    };
+
+    // Software pipeline over tiles: iteration j forms tile j + 1's scores on the matrix cores
+    // while the vector ALUs form tile j's probabilities, then runs tile j's PV and swaps tile
+    // j + 1's partial scores. Ring protocol (4 slots): tile t lives in slot t % 4 and is
+    // issued three tiles before its scores are formed; at the first barrier of iteration j,
+    // tile j + 1 has landed and tile j - 1's slot (last read by the PV of iteration j - 1)
+    // is free for tile j + 3.
+    if (ntiles > 0) {
+        issue(0, 0);
+        if (ntiles > 1) issue(1, 1);
+        if (ntiles > 2) issue(2, 2);
+        if (ntiles > 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WLT) : "memory");   // tile 0 is in
+        else if (ntiles > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        f32x16 sc = exchange(scores(ring));
+        int j = 0;
+        for (; j + 1 < ntiles; ++j) {
+            if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WLT) : "memory");   // tile j + 1 is in
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (j + 3 < ntiles) issue(j + 3, (j + 3) % STAGES);
+            const f32x16 nxt = scores(ring + ((j + 1) % STAGES) * TILE_ELEMS);
+            uint32_t pk[8];
+            softmax(sc, kvalid_of(j), pk);
+            pv(ring + (j % STAGES) * TILE_ELEMS, pk);
+            sc = exchange(nxt);
+        }
+        uint32_t pk[8];
+        softmax(sc, kvalid_of(j), pk);
+        pv(ring + (j % STAGES) * TILE_ELEMS, pk);
     }
 
     agpr_settle(acc_o);
