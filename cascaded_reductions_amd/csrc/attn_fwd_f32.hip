@@ -9,7 +9,8 @@
 // Mapping (wave64, v_mfma_f32_16x16x4_f32):
 //  * a workgroup owns 16 query rows and NW waves (8 for D = 64, 4 for D = 128);
 //    wave w walks key tiles of 16
-//    keys t = w, w + NW, ... (an intra-block split of the key axis);
+//    keys t = w, w + NW, ... (an intra-block split of the key axis), loading tile
+//    t + NW's K and V into registers before it works on tile t;
 //  * scores are formed transposed, S^T = K Q^T, so that each lane holds one query
 //    row (lane % 16) and four keys (4 * (lane / 16) + r): the row statistics are
 //    lane-local plus a two-step butterfly over the lane groups;
@@ -65,20 +66,43 @@ __global__ __launch_bounds__(kNW * 64) void attn_fwd_f32_kernel(const float* __r
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kb = int64_t(wave) * 16; kb < Sk; kb += int64_t(kNW) * 16) {
-        // K operand: lane (key r16, group g) holds K[kb + r16][g*C + c].
-        f32x4 st = {0.f, 0.f, 0.f, 0.f};
-        {
-            const int64_t kj = kb + r16 < Sk ? kb + r16 : Sk - 1;
-            const float4* src = reinterpret_cast<const float4*>(kh + kj * D + g * C);
+    // K operand of a key tile: lane (key r16, group g) holds K[kb + r16][g*C + c]; V operand:
+    // lane holds V[kb + 4g + r][16b + r16] for key slot r and column block b. Keys past the
+    // axis re-read the last key (their scores are masked).
+    auto load_kv = [&](int64_t kb, float4 (&kf)[C / 4], float (&vf)[4][DB]) {
+        const int64_t kj = kb + r16 < Sk ? kb + r16 : Sk - 1;
+        const float4* src = reinterpret_cast<const float4*>(kh + kj * D + g * C);
 #pragma unroll
-            for (int c = 0; c < C / 4; ++c) {
-                float4 t = src[c];
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x, qf[4 * c + 0], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.y, qf[4 * c + 1], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.z, qf[4 * c + 2], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.w, qf[4 * c + 3], st, 0, 0, 0);
-            }
+        for (int c = 0; c < C / 4; ++c) kf[c] = src[c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t vj = kb + 4 * g + r < Sk ? kb + 4 * g + r : Sk - 1;
+            const float* vrow = vh + vj * D + r16;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) vf[r][b] = vrow[16 * b];
+        }
+    };
+
+    // The next tile's K and V are loaded before the current tile is processed, so one
+    // memory round trip overlaps the MFMA and softmax work of the tile before.
+    const int64_t kstep = int64_t(kNW) * 16;
+    float4 kf[C / 4];
+    float vf[4][DB];
+    int64_t kb = int64_t(wave) * 16;
+    if (kb < Sk) load_kv(kb, kf, vf);
+    for (; kb < Sk; kb += kstep) {
+        const bool more = kb + kstep < Sk;
+        float4 kn[C / 4];
+        float vn[4][DB];
+        if (more) load_kv(kb + kstep, kn, vn);
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C / 4; ++c) {
+            const float4 t = kf[c];
+            st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x, qf[4 * c + 0], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.y, qf[4 * c + 1], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.z, qf[4 * c + 2], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x4f32(t.w, qf[4 * c + 3], st, 0, 0, 0);
         }
         // st[r] = S[query q0 + r16][key kb + 4g + r] (unscaled).
         float x[4];
@@ -107,12 +131,17 @@ __global__ __launch_bounds__(kNW * 64) void attn_fwd_f32_kernel(const float* __r
         for (int b = 0; b < DB; ++b) acc[b] *= alpha;
         // O^T += V^T P^T, one MFMA per key slot r: lane group g contributes key kb + 4g + r.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t kj = kb + 4 * g + r < Sk ? kb + 4 * g + r : Sk - 1;
-            const float* vrow = vh + kj * D + r16;
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int b = 0; b < DB; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * b], p[r], acc[b], 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[r][b], p[r], acc[b], 0, 0, 0);
+        if (more) {
+#pragma unroll
+            for (int c = 0; c < C / 4; ++c) kf[c] = kn[c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int b = 0; b < DB; ++b) vf[r][b] = vn[r][b];
         }
     }
 
