@@ -67,6 +67,27 @@ def test_mla_scales(rf, scale):
     _check(rf, 1, 64, 257, 2, seed=61, scale=scale)
 
 
+@pytest.mark.parametrize("growth,nseg", [(12.0, 1), (60.0, 1), (60.0, 3)])
+def test_mla_growing_scores(rf, growth, nseg):
+    """Cache rows pushed along the heads' mean query direction, more for later tokens, so
+    every head's scores grow along the sequence by about `growth` (natural units): the
+    reference maximum moves again and again inside the software-pipelined tile loop."""
+    from synth import f32_to_bf16_bits
+    B, H, L = 1, 64, 640
+    q, kv, scale = mla_inputs(B, H, L, 64)
+    qf, kvf = _f(q), _f(kv)
+    qm = qf.mean(axis=1)                                     # [B, 576]
+    c = np.linspace(0.0, growth / (scale * (qm ** 2).sum()), L)
+    kv = f32_to_bf16_bits((kvf + c[None, :, None] * qm[:, None, :]).astype(np.float32))
+    dq, dkv = dev_bf16(q), dev_bf16(kv)
+    pm, ps, po = rf.mla_decode_split(dq, dkv, nseg, scale)
+    o, lse = rf.segment_merge(pm, ps, po, torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(qf, _f(kv), DV, scale)
+    assert_close(host(o).reshape(B, H, DV), ro, ATOL, RTOL, "O")
+    assert_close(host(lse).reshape(B, H), rl, ATOL, RTOL, "lse")
+
+
 def test_mla_automatic_segments(rf):
     q, kv, scale = mla_inputs(4, 128, 640, 62)
     o, lse = rf.mla_decode(dev_bf16(q), dev_bf16(kv), scale)
