@@ -276,7 +276,7 @@ rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t 
     RF_REQUIRE(scale == scale && scale - scale == 0.0f, RF_ERR_INVALID_ARGUMENT, "scale must be finite");
     int64_t nq, nkv, np, npo, nblk;
     RF_REQUIRE(prod({B, H, d_qk}, &nq) && prod({B, L, d_qk}, &nkv) && nkv < kMaxElems && prod({B, H, nseg}, &np) &&
-                   prod({np, d_v}, &npo) && npo < kMaxElems && prod({B, (H + 127) / 128, nseg}, &nblk) &&
+                   prod({np, d_v}, &npo) && npo < kMaxElems && prod({B, (H + 63) / 64, nseg}, &nblk) &&
                    nblk <= INT32_MAX,
                RF_ERR_UNSUPPORTED, "problem too large");
     RF_REQUIRE(!overlap(part_m, np * 4, q, nq * 2) && !overlap(part_m, np * 4, kv, nkv * 2) &&

@@ -235,7 +235,7 @@ RF_API rf_status rf_attn_decode(const void* q, const void* k, const void* v, int
  *   q        [B, H, 576] bf16.   kv  [B, L, 576] bf16.
  *   d_qk, d_v  must be 576 and 512.
  *   part_m, part_s  fp32, B*H*nseg elements each.  part_o  fp32, B*H*nseg*512 elements.
- *   Supported: B, H, L >= 1; H a multiple of 32; 1 <= nseg <= L; B*ceil(H/128)*nseg <= 2^31 - 1.
+ *   Supported: B, H, L >= 1; H a multiple of 32; 1 <= nseg <= L; B*ceil(H/64)*nseg <= 2^31 - 1.
  */
 RF_API rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t H, int64_t L,
                                      int64_t d_qk, int64_t d_v, int64_t nseg, float scale, float* part_m,
