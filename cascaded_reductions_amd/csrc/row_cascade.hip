@@ -21,9 +21,9 @@ namespace {
 using namespace cascade;
 
 // G lanes fold one row (G in {4, 8, 16, 32, 64}; 64 / G rows per wave): lane i of the group
-// absorbs elements 4i .. 4i+3 of every 4G-element stretch (four 16-byte loads in flight
-// when there is no payload), then the group's states are merged by xor shuffles within
-// the group, in a fixed order.
+// absorbs elements 4i .. 4i+3 of every 4G-element stretch (eight, or four for a large
+// state, streaming 16-byte loads in flight when there is no payload), then the group's
+// states are merged by xor shuffles within the group, in a fixed order.
 template <class Spec, int G>
 __device__ __forceinline__ typename Spec::State fold_row(const float* __restrict__ xr, const float* __restrict__ pr,
                                                          int64_t N, int li) {
@@ -36,15 +36,22 @@ __device__ __forceinline__ typename Spec::State fold_row(const float* __restrict
         for (int e = 0; e < 4; ++e) Spec::absorb(st, xs[e], int32_t(j0 + e), P ? pr + (j0 + e) * P : nullptr);
     };
     const bool vec = (N & 3) == 0;            // 16-byte loads need aligned rows
-    // Four loads in flight when only x is read; with a payload its loads already overlap.
-    const int64_t full4 = vec && P == 0 ? N / (4 * STRIDE) * (4 * STRIDE) : 0;
+    // Eight loads in flight when only x is read (nontemporal: the row is read once), four for
+    // a large state (top-k: its registers would cost occupancy); with a payload its loads
+    // already overlap.
+    constexpr int UN = sizeof(typename Spec::State) > 32 ? 4 : 8;
+    const int64_t full4 = vec && P == 0 ? N / (UN * STRIDE) * (UN * STRIDE) : 0;
     int64_t j0 = 4 * li;
-    for (; j0 < full4; j0 += 4 * STRIDE) {
-        float4 v[4];
+    for (; j0 < full4; j0 += UN * STRIDE) {
+        float4 v[UN];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(xr + j0 + u * STRIDE);
+        for (int u = 0; u < UN; ++u) {
+            typedef float fx4 __attribute__((ext_vector_type(4)));
+            const fx4 t = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(xr + j0 + u * STRIDE));
+            v[u] = make_float4(t[0], t[1], t[2], t[3]);
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) absorb4(v[u], j0 + u * STRIDE);
+        for (int u = 0; u < UN; ++u) absorb4(v[u], j0 + u * STRIDE);
     }
     const int64_t full = vec ? N / STRIDE * STRIDE : 0;
     for (; j0 < full; j0 += STRIDE) absorb4(*reinterpret_cast<const float4*>(xr + j0), j0);
