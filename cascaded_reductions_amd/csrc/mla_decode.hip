@@ -38,8 +38,6 @@
 // Partials: part_m holds each segment's reference in natural units, part_s and
 // part_o the sum and the unnormalised accumulator relative to it -- the same
 // triple the merge combines exactly whatever the reference is.
-#include <type_traits>
-
 #include "common.hpp"
 #include "launch.hpp"
 
