@@ -7,7 +7,7 @@
 // rounding has no incremental form (its inverse does not exist), so the cascade
 // runs as two launches on one stream (the explainer's multi-kernel level,
 // section 3.3):
-//  1. quant_rows: one workgroup per row keeps the row in registers, reduces the
+//  1. quant_rows: one wave per row keeps the row in registers, reduces the
 //     absolute maximum (an integer max over the bf16 magnitude bits), forms
 //     sigma = a / 448 and each code from the IEEE fp32 quotient x / sigma
 //     (reciprocal + one FMA correction, correctly rounded) with the hardware
@@ -36,7 +36,7 @@ namespace {
 
 // ------------------------------------------------------------------ 1. per-row quantisation
 
-constexpr int QT = 256;   // threads per row
+constexpr int QT = 256;   // threads per workgroup
 
 __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -57,51 +57,52 @@ __device__ __forceinline__ float div_rn(float x, float sigma, float r) {
     return __builtin_copysignf(fmaf(e, r, q0), x);
 }
 
-// One workgroup per row. NCT > 0: the row (at most NCT * QT chunks of 8 values) stays
-// in registers between the absmax pass and the quantisation pass; NCT == 0: the row is
-// read twice.
+// One wave per row, four rows per workgroup. NCT > 0: lane l holds chunks l, l + 64, ...
+// (at most NCT chunks of 8 values), all loaded before the first use so every 16-byte
+// load of the row is in flight at once, and the row stays in registers between the
+// absmax and the quantisation; NCT == 0: the row is streamed twice. The absmax is
+// reduced across the wave by xor shuffles: no LDS and no barrier.
+constexpr int QROWS = QT / 64;
+
+__device__ __forceinline__ uint32_t absmax8(const u32x4& t, uint32_t m) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        m = max(m, t[w] & 0x7FFFu);             // bf16 magnitude bits order like the magnitudes
+        m = max(m, (t[w] >> 16) & 0x7FFFu);
+    }
+    return m;
+}
+
 template <int NCT>
-__global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t K,
+__global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                         uint8_t* __restrict__ codes, float* __restrict__ xs) {
-    __shared__ uint32_t sm_max[QT / 64];
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const uint16_t* xr = x + row * K;
-    uint8_t* cr = codes + row * K;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = int64_t(blockIdx.x) * QROWS + (threadIdx.x >> 6);
+    if (row >= M) return;                      // whole waves only: no barrier follows
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * K);
+    uint2* cr = reinterpret_cast<uint2*>(codes + row * K);
     const int nch = int(K / 8);
 
-    auto absmax8 = [](const u32x4& t, uint32_t m) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            m = max(m, t[w] & 0x7FFFu);             // bf16 magnitude bits order like the magnitudes
-            m = max(m, (t[w] >> 16) & 0x7FFFu);
-        }
-        return m;
-    };
     uint32_t amax = 0;
     u32x4 v[NCT > 0 ? NCT : 1];
     if constexpr (NCT > 0) {
 #pragma unroll
         for (int i = 0; i < NCT; ++i) {
-            const int ch = tid + i * QT;
-            v[i] = ch < nch ? *reinterpret_cast<const u32x4*>(xr + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-            amax = absmax8(v[i], amax);
+            const int ch = lane + i * 64;
+            v[i] = ch < nch ? __builtin_nontemporal_load(xr + ch) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) amax = absmax8(v[i], amax);
     } else {
-        for (int ch = tid; ch < nch; ch += QT) amax = absmax8(*reinterpret_cast<const u32x4*>(xr + ch * 8), amax);
+        for (int ch = lane; ch < nch; ch += 64) amax = absmax8(xr[ch], amax);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = max(amax, uint32_t(__shfl_xor(int(amax), m, 64)));
-    if ((tid & 63) == 0) sm_max[tid >> 6] = amax;
-    __syncthreads();
-    amax = sm_max[0];
-#pragma unroll
-    for (int w = 1; w < QT / 64; ++w) amax = max(amax, sm_max[w]);
 
     const float a = bf16_to_f32(amax);
     const float sigma = a / 448.0f;            // IEEE fp32 division
     const float r = 1.0f / sigma;              // IEEE fp32 division (inf for a zero row; unused then)
-    if (tid == 0) xs[row] = sigma;
+    if (lane == 0) xs[row] = sigma;
 
     auto quant8 = [&](const u32x4& t, int ch) {
         uint32_t out0 = 0u, out1 = 0u;
@@ -115,16 +116,16 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
             out0 = codes4(q[0], q[1], q[2], q[3]);
             out1 = codes4(q[4], q[5], q[6], q[7]);
         }
-        *reinterpret_cast<uint2*>(cr + ch * 8) = make_uint2(out0, out1);
+        cr[ch] = make_uint2(out0, out1);
     };
     if constexpr (NCT > 0) {
 #pragma unroll
         for (int i = 0; i < NCT; ++i) {
-            const int ch = tid + i * QT;
+            const int ch = lane + i * 64;
             if (ch < nch) quant8(v[i], ch);
         }
     } else {
-        for (int ch = tid; ch < nch; ch += QT) quant8(*reinterpret_cast<const u32x4*>(xr + ch * 8), ch);
+        for (int ch = lane; ch < nch; ch += 64) quant8(xr[ch], ch);
     }
 }
 
@@ -212,45 +213,75 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
+    // One K slice = 32 code bytes of every row. Lane (row l32, half g) reads the 16 bytes
+    // [32p + 16g, +16) of its rows; after the exact bf16 conversion, bytes 0-7 feed the first
+    // K=16 MFMA of a pair and bytes 8-15 the second (the same slot-to-k map for both operands).
+    auto read_slice = [&](int st, int p, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
+        const uint8_t* sw = smem[st][0];
+        const uint8_t* sx = smem[st][1];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            ra[a] = *reinterpret_cast<const u32x4*>(sw + swz(wn * 128 + a * 32 + l32, 2 * p + g));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            rb[b] = *reinterpret_cast<const u32x4*>(sx + swz(wm * 64 + b * 32 + l32, 2 * p + g));
+    };
+    struct Operands {
+        bf16x8 alo[4], ahi[4], blo[2], bhi[2];
+    };
+    auto convert = [&](const u32x4 (&ra)[4], const u32x4 (&rb)[2], Operands& o) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            o.alo[a] = fp8x8_to_bf16(ra[a][0], ra[a][1]);
+            o.ahi[a] = fp8x8_to_bf16(ra[a][2], ra[a][3]);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            o.blo[b] = fp8x8_to_bf16(rb[b][0], rb[b][1]);
+            o.bhi[b] = fp8x8_to_bf16(rb[b][2], rb[b][3]);
+        }
+    };
+    auto mfmas = [&](const Operands& o) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.alo[a], o.blo[b], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.ahi[a], o.bhi[b], acc[a][b], 0, 0, 0);
+            }
+    };
+
+    // Software pipeline: the LDS reads of slice p+1 are issued before the MFMAs of slice p,
+    // and the step's barrier sits between the last slice's conversion and its MFMAs, so the
+    // first slice of the next stage is read while those MFMAs run. The stage a step's loads
+    // overwrite was last read before the previous step's barrier.
     const int64_t nk = K / BK;
     load(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    u32x4 ra[4], rb[2];
+    read_slice(0, 0, ra, rb);
     for (int64_t t = 0; t < nk; ++t) {
         const int st = int(t & 1);
         if (t + 1 < nk) load((t + 1) * BK, st ^ 1);
-        const uint8_t* sw = smem[st][0];
-        const uint8_t* sx = smem[st][1];
 #pragma unroll
-        for (int p = 0; p < BK / 32; ++p) {
-            // Lane (row l32, half g) reads the 16 code bytes [32p + 16g, +16) of its row and
-            // converts them exactly to bf16: bytes 0-7 feed the first K=16 MFMA of the pair,
-            // bytes 8-15 the second (the same slot-to-k map for both operands).
-            bf16x8 alo[4], ahi[4], blo[2], bhi[2];
+        for (int p = 0; p < BK / 32 - 1; ++p) {
+            u32x4 na[4], nb[2];
+            read_slice(st, p + 1, na, nb);
+            Operands o;
+            convert(ra, rb, o);
+            mfmas(o);
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int r = wn * 128 + a * 32 + l32;
-                const u32x4 raw = *reinterpret_cast<const u32x4*>(sw + swz(r, 2 * p + g));
-                alo[a] = fp8x8_to_bf16(raw[0], raw[1]);
-                ahi[a] = fp8x8_to_bf16(raw[2], raw[3]);
-            }
+            for (int a = 0; a < 4; ++a) ra[a] = na[a];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int r = wm * 64 + b * 32 + l32;
-                const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + swz(r, 2 * p + g));
-                blo[b] = fp8x8_to_bf16(raw[0], raw[1]);
-                bhi[b] = fp8x8_to_bf16(raw[2], raw[3]);
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[a], blo[b], acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[a], bhi[b], acc[a][b], 0, 0, 0);
-                }
+            for (int b = 0; b < 2; ++b) rb[b] = nb[b];
         }
+        Operands o;
+        convert(ra, rb, o);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if (t + 1 < nk) read_slice(st ^ 1, 0, ra, rb);
+        mfmas(o);
     }
 
     // acc[a][b][r] = C^T[n][m]: n = n0 + wn*128 + a*32 + (r/4)*8 + 4g + r%4, m = m0 + wm*64 + b*32 + l32.
@@ -316,16 +347,15 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes, float* x_scale,
                              hipStream_t stream) {
-    if (M > INT32_MAX || K / 8 > INT32_MAX) return hipErrorInvalidValue;
-    const int64_t nct = ceil_div(K / 8, QT);
-    const dim3 grid{unsigned(M), 1u, 1u};
-    switch (nct) {
-        case 1: hipLaunchKernelGGL(quant_rows_kernel<1>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
-        case 2: hipLaunchKernelGGL(quant_rows_kernel<2>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
-        case 3: hipLaunchKernelGGL(quant_rows_kernel<3>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
-        case 4: hipLaunchKernelGGL(quant_rows_kernel<4>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
-        default: hipLaunchKernelGGL(quant_rows_kernel<0>, grid, dim3(QT), 0, stream, x, K, codes, x_scale); break;
-    }
+    if (ceil_div(M, QROWS) > INT32_MAX || K / 8 > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t nct = ceil_div(K / 8, 64);   // chunks of 8 values per lane
+    const dim3 grid{unsigned(ceil_div(M, QROWS)), 1u, 1u};
+    if (nct <= 1) hipLaunchKernelGGL(quant_rows_kernel<1>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    else if (nct <= 2) hipLaunchKernelGGL(quant_rows_kernel<2>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    else if (nct <= 4) hipLaunchKernelGGL(quant_rows_kernel<4>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    else if (nct <= 8) hipLaunchKernelGGL(quant_rows_kernel<8>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    else if (nct <= 16) hipLaunchKernelGGL(quant_rows_kernel<16>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    else hipLaunchKernelGGL(quant_rows_kernel<0>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
     return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ def _check(rf, x, wq, ws, use_workspace=False):
     (1, 1, 128),
     (300, 520, 1024),
     (513, 257, 384),
+    (70, 90, 2048),       # four 8-value chunks per lane in the row quantiser
+    (9, 33, 8192),        # sixteen chunks per lane: the longest rows kept in registers
 ])
 def test_quant_gemm_shapes(rf, M, N, K):
     x, wq, ws = quant_inputs(M, N, K, seed=700 + M + N + K)
