@@ -372,7 +372,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         using I4 = std::integral_constant<int, 4>;
         using I5 = std::integral_constant<int, 5>;
         using F = std::false_type;
-        u32x8 pka, pkb;                          // probabilities of even / odd tiles
+        u32x8 pka{}, pkb{};                      // probabilities of even / odd tiles
         const int nst = nsteps - 1;              // steps with a successor
         if (nst > 0) step(0, I0{}, std::true_type{}, sa, sb, pkb, pka);
         int j = 1;

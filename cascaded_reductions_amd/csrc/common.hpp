@@ -86,26 +86,18 @@ __device__ __forceinline__ float row8_sum(float v) {
 // including loads of buffers that are only used later. The caller orders them with
 // an explicit "s_waitcnt vmcnt(N)" and a barrier (vmcnt retires loads in issue order,
 // so loads the compiler does not know of can only make its own waits stricter).
+// The LDS base goes to M0 through the "{m0}" operand constraint, so the compiler sets M0
+// itself and knows the value it holds.
 __device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds_base)));
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(base), "v"(gptr)
-        : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(base) : "memory");
 }
 
 // The same with a wave-uniform 64-bit global base (SGPR pair) and a per-lane 32-bit
 // byte offset: the address costs no vector instruction.
 __device__ __forceinline__ void lds_dma16_sb(const void* gbase, uint32_t voff_bytes, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
-        :
-        : "s"(lds_base), "v"(voff_bytes), "s"(gbase)
-        : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff_bytes), "s"(gbase), "{m0}"(lds_base) : "memory");
 }
 
 // LDS byte address of a __shared__ object (wave-uniform when the pointer is).

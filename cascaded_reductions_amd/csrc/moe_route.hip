@@ -199,16 +199,18 @@ __global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __rest
 
 }
 
-// Phase 2: sixteen lanes per token (4 tokens per wave, 16 per workgroup); lane q of a
-// token owns experts [q * NEB, q * NEB + NEB).
+// Phase 2: sixteen lanes per token (4 tokens per wave, one wave per workgroup, so 2048
+// tokens spread over 512 workgroups); lane q of a token owns experts [q * NEB, q * NEB + NEB).
+constexpr int RED_T = 64;             // threads per reduce workgroup
+
 template <int NEB, int K>
-__global__ __launch_bounds__(256) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
+__global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
                                                          int k, int32_t* __restrict__ idx, float* __restrict__ wout,
                                                          float* __restrict__ scores) {
     constexpr int E = NEB * 16;
     const int tid = threadIdx.x;
     const int q = tid & 15;
-    const int64_t t_out = int64_t(blockIdx.x) * 16 + (tid >> 4);
+    const int64_t t_out = int64_t(blockIdx.x) * (RED_T / 16) + (tid >> 4);
     const bool valid = t_out < T;
     float ts[K];
     int ti[K];
@@ -288,13 +290,13 @@ hipError_t launch_e(int k, const MoeGeom& g, int swz, hipStream_t stream, const 
                        part);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid2{unsigned(ceil_div(T, int64_t(16))), 1u, 1u};
+    const dim3 grid2{unsigned(ceil_div(T, int64_t(RED_T / 16))), 1u, 1u};
     // A top-2 fast path; any other k up to 8 keeps an 8-entry list.
     if (k == 2)
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(256), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(RED_T), 0, stream, part, T, g.nranges, k, idx, wout,
                            scores);
     else
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(256), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(RED_T), 0, stream, part, T, g.nranges, k, idx, wout,
                            scores);
     return hipGetLastError();
 }
@@ -308,7 +310,7 @@ size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E) {
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd, int E, int k,
                             int32_t* idx, float* w, float* scores, void* workspace, hipStream_t stream) {
     const MoeGeom g = moe_geom(T, Hd, E);
-    if (g.ntb * g.nranges > INT32_MAX || ceil_div(T, int64_t(16)) > INT32_MAX) return hipErrorInvalidValue;
+    if (g.ntb * g.nranges > INT32_MAX || ceil_div(T, int64_t(RED_T / 16)) > INT32_MAX) return hipErrorInvalidValue;
     const int CH = E / 8;
     const int swz = (CH >= 8 && (CH & (CH - 1)) == 0) ? 6 : 0;
     float* part = static_cast<float*>(workspace);
