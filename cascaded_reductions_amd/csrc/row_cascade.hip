@@ -53,6 +53,36 @@ __device__ __forceinline__ typename Spec::State fold_row(const float* __restrict
 #pragma unroll
         for (int u = 0; u < UN; ++u) absorb4(v[u], j0 + u * STRIDE);
     }
+    // With a payload of P <= 4 values, UPW stretches of x and payload (1 + P 16-byte loads
+    // each) are loaded before any is absorbed, so 8-10 loads are in flight per lane; the
+    // elements are absorbed in the same order as one stretch at a time.
+    constexpr int UPW = P == 0 ? 1 : P <= 1 ? 4 : P <= 2 ? 3 : P <= 4 ? 2 : 1;
+    if constexpr (UPW > 1) {
+        typedef float fx4 __attribute__((ext_vector_type(4)));
+        const int64_t fullp = vec ? N / (UPW * STRIDE) * (UPW * STRIDE) : 0;
+        for (; j0 < fullp; j0 += UPW * STRIDE) {
+            fx4 xv[UPW];
+            float pv[UPW][4 * P];
+#pragma unroll
+            for (int u = 0; u < UPW; ++u) {
+                const int64_t j = j0 + u * STRIDE;
+                xv[u] = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(xr + j));
+#pragma unroll
+                for (int c = 0; c < P; ++c) {
+                    // Cached loads: lane i's P 16-byte loads of a stretch share cache lines
+                    // with lane i + 1's, so a streaming hint would fetch each line again.
+                    const fx4 t = *reinterpret_cast<const fx4*>(pr + j * P + 4 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[u][4 * c + e] = t[e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UPW; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Spec::absorb(st, xv[u][e], int32_t(j0 + u * STRIDE + e), &pv[u][e * P]);
+        }
+    }
     const int64_t full = vec ? N / STRIDE * STRIDE : 0;
     for (; j0 < full; j0 += STRIDE) absorb4(*reinterpret_cast<const float4*>(xr + j0), j0);
     for (int64_t j = full + li; j < N; j += G) Spec::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
