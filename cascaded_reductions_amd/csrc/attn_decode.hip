@@ -146,7 +146,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const uint16_t* __rest
     }
 }
 
-// One wave per row; lane owns D/64 output columns.
+// One wave per row. D = 512: lane l owns the column groups [4l + 256v, +4), v = 0, 1, so
+// every 16-byte load instruction of the wave reads 1 KiB of contiguous partials, and the
+// loads of four segments are issued before their products are added. Smaller D: lane owns
+// D/64 adjacent columns. Either way each column adds the segments in segment order.
 template <int D>
 __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restrict__ part_m,
                                                             const float* __restrict__ part_s,
@@ -154,12 +157,14 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
                                                             int64_t rows, int nseg, int out_bf16,
                                                             void* __restrict__ out, float* __restrict__ lse) {
     constexpr int PER = D / 64;
+    constexpr bool GROUPED = PER % 4 == 0;    // column groups of 4 at a stride of 256
+    constexpr int NV = GROUPED ? PER / 4 : 1;
     const int lane = threadIdx.x & 63;
     const int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
     const float* pm = part_m + r * nseg;
     const float* ps = part_s + r * nseg;
-    const float* po = part_o + r * nseg * D + lane * PER;
+    const float* po = part_o + r * nseg * D + (GROUPED ? 4 * lane : lane * PER);
 
     float M = kNegInf;
     for (int t = lane; t < nseg; t += 64) M = fmaxf(M, pm[t]);
@@ -169,6 +174,16 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
     float S = 0.f, O[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[i] = 0.f;
+    // O[4v + e] is column 4 * lane + 256 v + e when GROUPED, else column lane * PER + i.
+    auto add_grouped = [&](float wt, const float4 (&x)[NV]) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            O[4 * v + 0] = fmaf(wt, x[v].x, O[4 * v + 0]);
+            O[4 * v + 1] = fmaf(wt, x[v].y, O[4 * v + 1]);
+            O[4 * v + 2] = fmaf(wt, x[v].z, O[4 * v + 2]);
+            O[4 * v + 3] = fmaf(wt, x[v].w, O[4 * v + 3]);
+        }
+    };
     for (int t0 = 0; t0 < nseg; t0 += 64) {
         const int t = t0 + lane;
         float w = 0.f;
@@ -178,18 +193,28 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
             S += w * ps[t];
         }
         const int n = nseg - t0 < 64 ? nseg - t0 : 64;
-        for (int tt = 0; tt < n; ++tt) {
+        int tt = 0;
+        if constexpr (GROUPED) {
+            constexpr int UB = 4;                 // segments whose loads are in flight together
+            for (; tt + UB <= n; tt += UB) {
+                float4 x[UB][NV];
+#pragma unroll
+                for (int u = 0; u < UB; ++u)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        x[u][v] = *reinterpret_cast<const float4*>(po + int64_t(t0 + tt + u) * D + 256 * v);
+#pragma unroll
+                for (int u = 0; u < UB; ++u) add_grouped(__shfl(w, tt + u, 64), x[u]);
+            }
+        }
+        for (; tt < n; ++tt) {
             const float wt = __shfl(w, tt, 64);
             const float* src = po + int64_t(t0 + tt) * D;
-            if constexpr (PER % 4 == 0) {
+            if constexpr (GROUPED) {
+                float4 x[NV];
 #pragma unroll
-                for (int i4 = 0; i4 < PER / 4; ++i4) {
-                    const float4 x = *reinterpret_cast<const float4*>(src + 4 * i4);
-                    O[4 * i4 + 0] = fmaf(wt, x.x, O[4 * i4 + 0]);
-                    O[4 * i4 + 1] = fmaf(wt, x.y, O[4 * i4 + 1]);
-                    O[4 * i4 + 2] = fmaf(wt, x.z, O[4 * i4 + 2]);
-                    O[4 * i4 + 3] = fmaf(wt, x.w, O[4 * i4 + 3]);
-                }
+                for (int v = 0; v < NV; ++v) x[v] = *reinterpret_cast<const float4*>(src + 256 * v);
+                add_grouped(wt, x);
             } else if constexpr (PER == 2) {
                 const float2 x = *reinterpret_cast<const float2*>(src);
                 O[0] = fmaf(wt, x.x, O[0]);
@@ -202,14 +227,29 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
     S = wave_sum(S);
     const bool empty = !(S > 0.f);
     const float inv = empty ? 0.f : 1.f / S;
+    if constexpr (GROUPED) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const float val = empty ? 0.f : O[i] * inv;
-        const int64_t idx = r * D + lane * PER + i;
-        if (out_bf16)
-            static_cast<uint16_t*>(out)[idx] = uint16_t(f32_to_bf16_rne(val));
-        else
-            static_cast<float*>(out)[idx] = val;
+        for (int v = 0; v < NV; ++v) {
+            float val[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = empty ? 0.f : O[4 * v + e] * inv;
+            const int64_t idx = r * D + 4 * lane + 256 * v;
+            if (out_bf16)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
+                    make_uint2(pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3]));
+            else
+                *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(val[0], val[1], val[2], val[3]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const float val = empty ? 0.f : O[i] * inv;
+            const int64_t idx = r * D + lane * PER + i;
+            if (out_bf16)
+                static_cast<uint16_t*>(out)[idx] = uint16_t(f32_to_bf16_rne(val));
+            else
+                static_cast<float*>(out)[idx] = val;
+        }
     }
     if (lse && lane == 0) lse[r] = empty ? kNegInf : M + __logf(S);
 }
