@@ -147,9 +147,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const uint16_t* __rest
 }
 
 // One wave per row. D = 512: lane l owns the column groups [4l + 256v, +4), v = 0, 1, so
-// every 16-byte load instruction of the wave reads 1 KiB of contiguous partials, and the
-// loads of four segments are issued before their products are added. Smaller D: lane owns
-// D/64 adjacent columns. Either way each column adds the segments in segment order.
+// every 16-byte load instruction of the wave reads 1 KiB of contiguous partials. Smaller D:
+// lane owns D/64 adjacent columns. For D = 512 and 128 the loads of four segments are
+// issued before their products are added; each column adds the segments in segment order.
 template <int D>
 __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restrict__ part_m,
                                                             const float* __restrict__ part_s,
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
         }
         const int n = nseg - t0 < 64 ? nseg - t0 : 64;
         int tt = 0;
+        constexpr int UB = 4;                     // segments whose loads are in flight together
         if constexpr (GROUPED) {
-            constexpr int UB = 4;                 // segments whose loads are in flight together
             for (; tt + UB <= n; tt += UB) {
                 float4 x[UB][NV];
 #pragma unroll
@@ -205,6 +205,18 @@ __global__ __launch_bounds__(256) void segment_merge_kernel(const float* __restr
                         x[u][v] = *reinterpret_cast<const float4*>(po + int64_t(t0 + tt + u) * D + 256 * v);
 #pragma unroll
                 for (int u = 0; u < UB; ++u) add_grouped(__shfl(w, tt + u, 64), x[u]);
+            }
+        } else if constexpr (PER == 2) {
+            for (; tt + UB <= n; tt += UB) {
+                float2 x[UB];
+#pragma unroll
+                for (int u = 0; u < UB; ++u) x[u] = *reinterpret_cast<const float2*>(po + int64_t(t0 + tt + u) * D);
+#pragma unroll
+                for (int u = 0; u < UB; ++u) {
+                    const float wt = __shfl(w, tt + u, 64);
+                    O[0] = fmaf(wt, x[u].x, O[0]);
+                    O[1] = fmaf(wt, x[u].y, O[1]);
+                }
             }
         }
         for (; tt < n; ++tt) {
