@@ -152,7 +152,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 }
 
 // LDS row of 128 bytes = 8 chunks of 16 bytes, chunk index XOR-swizzled by row.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// The LDS serves a wave's 16-byte reads 16 lanes (256 bytes, all 64 banks) per cycle, and
+// the 16 lanes of a read group take 16 consecutive rows at one logical chunk: rows r and
+// r + 1 differ in their 128-byte half of a bank row, and (row >> 1) & 7 gives the eight
+// even (or odd) rows eight distinct chunks, so the group is conflict-free. (An XOR with
+// row & 7 repeats every 8 rows and put rows r and r + 8 on the same banks.)
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so workgroup b runs
 // on XCD b % 8; renumbering makes each XCD own a contiguous range of logical tiles. The
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
 
     // Global -> LDS without registers (global_load_lds_dwordx4): one wave instruction
     // fills 1 KiB of LDS = 8 rows of 128 bytes, lane i landing in row i/8, physical
-    // chunk i%8; the lane therefore fetches logical chunk (i%8) ^ (row & 7).
+    // chunk i%8; the lane therefore fetches logical chunk (i%8) ^ ((row >> 1) & 7).
     // Waves 0-3 fill the W tile, waves 4-7 the X tile, 8 instructions each.
     const int which = wave >> 2;
     const uint8_t* gsrc = which ? xq : wq;
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
         for (int j = 0; j < 8; ++j) {
             const int r0 = ((wave & 3) * 8 + j) * 8;
             const int r = r0 + (lane >> 3);
-            const int ch = (lane & 7) ^ (r & 7);
+            const int ch = (lane & 7) ^ ((r >> 1) & 7);
             int64_t gr = base_row + r;
             gr = gr < lim ? gr : lim - 1;
             __builtin_amdgcn_global_load_lds(
