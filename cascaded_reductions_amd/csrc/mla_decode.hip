@@ -73,8 +73,18 @@ __device__ __forceinline__ bf16x4_t read_tr16(const uint16_t* p) {
 }
 
 // Element offset of logical 8-element chunk c of token row r inside a tile: the chunk
-// index is XOR-swizzled with r & 7 (it stays inside its aligned group of 8 chunks).
-__device__ __forceinline__ int tile_off(int r, int c) { return r * DQK + ((c ^ (r & 7)) << 3); }
+// index is XOR-swizzled with row_swz(r) < 8 (it stays inside its aligned group of 8
+// chunks). The LDS serves 256 bytes per cycle, and a row is 1152 bytes, so rows of one
+// parity share the 128-byte bank halves. The score reads of a 16-lane group take rows
+// 8a + 4tb + b (a, b in 0..3) at one chunk, and the transposed V reads of a 32-lane group
+// take rows 8a' + b + 4hi at two adjacent chunks, with a' in {0, 1} or {0, 2} depending
+// on how the hardware pairs the lane groups. Chunk bit 0 = row bit 3, bit 1 = row bit 1,
+// bit 2 = row bit 3 ^ row bit 4 gives every row of one parity its own banks in each of
+// these groups (an XOR with r & 7 would put rows 8 apart on the same ones).
+__device__ __forceinline__ int row_swz(int r) {
+    return ((r >> 3) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 2);
+}
+__device__ __forceinline__ int tile_off(int r, int c) { return r * DQK + ((c ^ row_swz(r)) << 3); }
 
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t H, int64_t L,
@@ -108,7 +118,7 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // Tile j of the segment into ring slot `slot`, by waves 0-3: wave load i (i = wave +
     // NLD * w) covers physical chunks [64 i, 64 i + 64) of the tile, so lane `lane` lands in
     // token row r = (64 i + lane) / RCH at physical chunk pc and fetches the logical chunk
-    // pc ^ (r & 7) that the read side expects there. A tile that runs past the segment
+    // pc ^ row_swz(r) that the read side expects there. A tile that runs past the segment
     // re-reads its last token for the rows beyond it (their weights are zeroed).
     const bool loader = wave < NLD;
     uint32_t goff[WLT];
@@ -116,7 +126,7 @@ void mla_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int w = 0; w < WLT; ++w) {
         const int p = (wave % NLD + NLD * w) * 64 + lane;
         const int r = p / RCH;
-        const int lc = (p - r * RCH) ^ (r & 7);
+        const int lc = (p - r * RCH) ^ row_swz(r);
         goff[w] = uint32_t(r * DQK + lc * 8) * 2u;
     }
     const uint32_t ring_lds = lds_addr(ring);
