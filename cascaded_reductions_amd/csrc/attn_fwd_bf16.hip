@@ -40,6 +40,7 @@
 //    XCD's L2 once.
 #include <type_traits>
 
+#include "attn_tiles.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,23 +65,6 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
 }
 
-// LDS chunk swizzles. The LDS serves 256 bytes per cycle: a 16-lane group of 16-byte K
-// reads (rows l32 = 16i .. 16i + 15 at one logical chunk) and a 32-lane group of 8-byte
-// transposed V reads (4 lanes on each of 8 key rows, two adjacent chunks per row; the
-// hardware may pair lane groups 0 + 1 or 0 + 2). At D = 64 a row is 128 bytes, so rows
-// of one parity share bank halves; at D = 128 a row is a whole bank row. The XOR masks
-// below give every row of such a group its own banks (an XOR with row & 7 repeats every
-// 8 rows and put rows 8 apart on the same banks).
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    if constexpr (D == 64) return (row >> 1) & 7;
-    else return row & 15;
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int key) {
-    if constexpr (D == 64) return (((key >> 2) & 1) << 1) | (((key >> 1) & 1) << 2);
-    else return (((key >> 2) & 1) << 1) | ((key & 1) << 2) | (((key >> 1) & 1) << 3);
-}
 
 template <int D, int STAGES, bool EXACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1)))
@@ -157,7 +141,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
     for (int l = 0; l < WL; ++l) {
         const int row = l * RPW + lane / CH;
         const int pc = lane % CH;
-        const int lc = ld_kind ? (pc ^ v_swz<D>(row)) : (pc ^ k_swz<D>(row));
+        const int lc = ld_kind ? (pc ^ attn_v_swz<D>(row)) : (pc ^ attn_k_swz<D>(row));
         ld_off[l] = uint32_t(row * D + lc * 8) * 2u;
     }
     const uint32_t ld_lds0 = lds_addr(smem) + uint32_t(((ld_kind ? STAGES * SLOT : 0) + ld_half * TILE) * 2);
@@ -189,7 +173,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
     // Read-side LDS element offsets (constant across steps).
     int k_off[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) k_off[c] = l32 * D + (((2 * c + h) ^ k_swz<D>(l32)) << 3);
+    for (int c = 0; c < NC; ++c) k_off[c] = l32 * D + (((2 * c + h) ^ attn_k_swz<D>(l32)) << 3);
     int v_off[2][DB][2];
     {
         const int j16 = lane & 15;
@@ -201,8 +185,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                 const int d = 32 * b + 16 * (l32 >> 4) + 4 * (j16 & 3);
                 const int key0 = kc * 16 + 4 * h + (j16 >> 2);
                 const int key1 = key0 + 8;
-                v_off[kc][b][0] = key0 * D + (((d >> 3) ^ v_swz<D>(key0)) << 3) + (d & 7);
-                v_off[kc][b][1] = key1 * D + (((d >> 3) ^ v_swz<D>(key1)) << 3) + (d & 7);
+                v_off[kc][b][0] = key0 * D + (((d >> 3) ^ attn_v_swz<D>(key0)) << 3) + (d & 7);
+                v_off[kc][b][1] = key1 * D + (((d >> 3) ^ attn_v_swz<D>(key1)) << 3) + (d & 7);
             }
     }
 

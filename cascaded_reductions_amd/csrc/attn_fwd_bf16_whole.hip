@@ -14,6 +14,7 @@
 // The LDS layout and its XOR swizzles are those of the incremental kernel.
 // NT (the number of key tiles) is a template parameter so that the score array
 // stays in registers.
+#include "attn_tiles.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -70,7 +71,7 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             const int li = i - kind * NT * WL;       // wave load within the K or V array
             const int row = li * RPW + lane / CH;    // key row of this lane
             const int pc = lane % CH;
-            const int lc = kind ? (pc ^ ((row & 3) << 1)) : (pc ^ (row & 7));
+            const int lc = kind ? (pc ^ attn_v_swz<D>(row)) : (pc ^ attn_k_swz<D>(row));
             const int grow = row < Sk ? row : Sk - 1;
             const uint16_t* src = (kind ? vh_ptr : kh_ptr) + int64_t(grow) * D + lc * 8;
             lds_dma16(src, smem + kind * NT * TILE + li * RPW * D);
@@ -102,7 +103,7 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + l32 * D + (((2 * c + h) ^ (l32 & 7)) << 3));
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + l32 * D + (((2 * c + h) ^ attn_k_swz<D>(l32)) << 3));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[c], acc, 0, 0, 0);
         }
         s[t] = acc;
@@ -159,8 +160,8 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 const int d = 32 * b + 16 * (l32 >> 4) + 4 * (j16 & 3);
                 const int key0 = kc * 16 + 4 * h + (j16 >> 2);
                 const int key1 = key0 + 8;
-                const bf16x4_t lo = read_tr16(vt + key0 * D + (((d >> 3) ^ ((key0 & 3) << 1)) << 3) + (d & 7));
-                const bf16x4_t hi = read_tr16(vt + key1 * D + (((d >> 3) ^ ((key1 & 3) << 1)) << 3) + (d & 7));
+                const bf16x4_t lo = read_tr16(vt + key0 * D + (((d >> 3) ^ attn_v_swz<D>(key0)) << 3) + (d & 7));
+                const bf16x4_t hi = read_tr16(vt + key1 * D + (((d >> 3) ^ attn_v_swz<D>(key1)) << 3) + (d & 7));
                 const bf16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
                                                                     __builtin_bit_cast(bf16x8, pb), acc_o[b], 0, 0, 0);
