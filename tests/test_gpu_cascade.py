@@ -28,7 +28,7 @@ def test_logsumexp(rf, R, N):
 
 
 @pytest.mark.parametrize("R,N", SHAPES)
-@pytest.mark.parametrize("P", [1, 4, 16])
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16])
 def test_softmax_weighted(rf, R, N, P):
     x = _x(R, N, 20 + N + P)
     p = np.random.default_rng(21 + N).standard_normal((R, N, P)).astype(np.float32)
