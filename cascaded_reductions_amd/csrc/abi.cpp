@@ -228,6 +228,10 @@ rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B,
                    rows <= INT32_MAX,
                RF_ERR_UNSUPPORTED, "tensor too large");
     if (nseg == 0) nseg = rf_attn_decode_segments(rows, L, 0);
+    int64_t nparts;
+    RF_REQUIRE(nseg == 1 || (prod({rows, nseg}, &nparts) && nparts <= INT32_MAX), RF_ERR_UNSUPPORTED,
+               "B*H*nseg must be <= 2^31 - 1 when the key axis is split (got %lld rows x %lld segments)",
+               (long long)rows, (long long)nseg);
     const uint64_t oes = out_dt == RF_F32 ? 4 : 2;
     RF_REQUIRE(!overlap(o, nq * oes, q, nq * 2) && !overlap(o, nq * oes, k, nkv * 2) &&
                    !overlap(o, nq * oes, v, nkv * 2) && !overlap(lse, rows * 4, q, nq * 2) &&

@@ -55,7 +55,7 @@ struct LogSumExp {
         if (x > st.m) {                                   // the running max moves: rescale s
             st.s = st.s * __expf(st.m - x) + 1.f;        // (exp(-inf) = 0 for the first element)
             st.m = x;
-        } else {
+        } else if (x != kNegInf) {                        // exp(-inf) adds nothing (and -inf - -inf is NaN)
             st.s += __expf(x - st.m);
         }
     }
@@ -84,6 +84,7 @@ struct SoftmaxWeighted {
         return st;
     }
     __device__ static void absorb(State& st, float x, int32_t, const float* v) {
+        if (x == kNegInf) return;                         // a masked element adds nothing
         const float m = fmaxf(st.m, x);
         const float alpha = st.m == kNegInf ? 0.f : __expf(st.m - m);
         const float p = __expf(x - m);
@@ -156,22 +157,23 @@ struct TopK {
 // pairwise rule of Chan, Golub and LeVeque).
 struct MeanVar {
     struct State {
-        float n, mean, m2;
+        uint32_t n;          // an integer count: a float one stops growing at 2^24
+        float mean, m2;
     };
     static constexpr int kPayload = 0;
-    __device__ static State identity() { return {0.f, 0.f, 0.f}; }
+    __device__ static State identity() { return {0u, 0.f, 0.f}; }
     __device__ static void absorb(State& st, float x, int32_t, const float*) {
-        st.n += 1.f;
+        st.n += 1u;
         const float d = x - st.mean;
-        st.mean += d / st.n;
+        st.mean += d / float(st.n);
         st.m2 += d * (x - st.mean);
     }
     __device__ static State combine(const State& a, const State& b) {
-        const float n = a.n + b.n;
-        if (n == 0.f) return identity();
+        const uint32_t n = a.n + b.n;
+        if (n == 0u) return identity();
         const float d = b.mean - a.mean;
-        const float fb = b.n / n;
-        return {n, a.mean + d * fb, a.m2 + b.m2 + d * d * a.n * fb};
+        const float fb = float(b.n) / float(n);
+        return {n, a.mean + d * fb, a.m2 + b.m2 + d * d * float(a.n) * fb};
     }
 };
 

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void mean_var_kernel(const float* __restrict__
     const auto st = fold_row<MeanVar, G>(x + r * N, nullptr, N, li);
     if (li == 0) {
         out[r * 2] = st.mean;
-        out[r * 2 + 1] = st.m2 / st.n;
+        out[r * 2 + 1] = st.m2 / float(st.n);
     }
 }
 

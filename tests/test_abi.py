@@ -234,3 +234,6 @@ def test_decode_one_call_validation(lib):
     assert call(o=P) == INVALID                               # o over q
     need = ws(2, 4, 300, 128, 3)
     assert call(ws_bytes=need, wsp=P4) == INVALID             # workspace over o
+    # 2^22 rows x 1024 segments: more split waves than the launch can index, refused on the host
+    assert d(P, P2, P3, 1 << 22, 1, 1024, 64, 1024, 0.1, 1, P4, None, P5, 1 << 40, None) == UNSUPPORTED
+    assert b"nseg" in lib.rf_last_error()

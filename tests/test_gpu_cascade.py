@@ -60,3 +60,35 @@ def test_deterministic(rf):
     b = rf.row_cascade("mean_var", x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def _masked(R, N, seed):
+    """Scores with -inf (masked) stretches: row 0 is masked except for its last element,
+    row 1 masks the first 64 elements (a whole first stretch for every lane of a small
+    group), row 2 masks every other 16-element block, the rest are unmasked."""
+    x = _x(R, N, seed)
+    x[0, :-1] = -np.inf
+    x[1, :64] = -np.inf
+    for j0 in range(0, N, 32):
+        x[2, j0:j0 + 16] = -np.inf
+    return x
+
+
+@pytest.mark.parametrize("R,N", [(4, 100), (4, 256), (3, 1000), (4, 4099)])
+def test_logsumexp_masked(rf, R, N):
+    x = _masked(R, N, 60 + N)
+    got = host(rf.row_cascade("logsumexp", dev_f32(x)))
+    assert np.isfinite(got).all()
+    assert_close(got, cascade.logsumexp(x), ATOL, RTOL, "lse")
+
+
+@pytest.mark.parametrize("R,N", [(4, 100), (4, 256), (3, 1000), (4, 4099)])
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_softmax_weighted_masked(rf, R, N, P):
+    x = _masked(R, N, 70 + N + P)
+    p = np.random.default_rng(71 + N).standard_normal((R, N, P)).astype(np.float32)
+    got = host(rf.row_cascade("softmax_weighted", dev_f32(x), dev_f32(p)))
+    assert np.isfinite(got).all()
+    assert_close(got, cascade.softmax_weighted(x, p), ATOL, RTOL, "o")
+    # the row masked except for its last element returns that element's payload
+    np.testing.assert_array_equal(got[0], p[0, -1].astype(np.float64))
