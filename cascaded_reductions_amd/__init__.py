@@ -14,12 +14,14 @@ import os
 
 __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16", "RF_ATTN_AUTO", "RF_ATTN_INCREMENTAL", "RF_ATTN_WHOLE_ROW",
-    "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_segments",
+    "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_noalloc",
+    "attn_decode_segments",
     "mla_decode_split", "mla_decode", "row_cascade",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+ABI_VERSION = 3
 RF_F32, RF_BF16 = 0, 1
 _STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARGUMENT", 2: "RF_ERR_UNSUPPORTED",
            3: "RF_ERR_BUFFER_TOO_SMALL", 4: "RF_ERR_DEVICE"}
@@ -50,6 +52,7 @@ _SIGS = {
     "rf_attn_decode_segments": ([_I64, _I64, _I64], _I64),
     "rf_attn_decode_workspace_size": ([_I64, _I64, _I64, _I64, _I64], _SZ),
     "rf_attn_decode": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _c.c_int, _P, _P, _P, _SZ, _P], _c.c_int),
+    "rf_attn_decode_noalloc": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_row_cascade": ([_c.c_int, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -70,7 +73,7 @@ def load():
         for name, (args, res) in _SIGS.items():
             fn = getattr(lib, name)
             fn.argtypes, fn.restype = args, res
-        if lib.rf_abi_version() != 2:
+        if lib.rf_abi_version() != ABI_VERSION:
             raise RFError(-1, f"unexpected ABI version {lib.rf_abi_version()}")
         _lib = lib
     return _lib
@@ -244,6 +247,28 @@ def attn_decode(q, k, v, nseg: int | None = None, scale: float | None = None, ou
     _check(load().rf_attn_decode(_ptr(q), _ptr(k), _ptr(v), B, H, L, D, n, float(scale),
                                  RF_F32 if out_dtype == torch.float32 else RF_BF16, _ptr(out), _ptr(lse), _ptr(ws),
                                  need, _stream(q)))
+    return out, lse
+
+
+def attn_decode_noalloc(q, k, v, out, lse, nseg: int | None = None, scale: float | None = None):
+    """rf_attn_decode_noalloc: decode attention with the partials in the library's static
+    device scratch (no workspace and no allocation in the call; the caller passes out
+    [B,H,D] bf16 or fp32 and lse [B,H] fp32). Concurrent calls on one GPU race on the scratch."""
+    torch = _torch()
+    B, H, D = q.shape
+    L = k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, H, L, D))
+    _need(v, "v", torch.bfloat16, (B, H, L, D))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _need(out, "out", out.dtype, (B, H, D))
+    _need(lse, "lse", torch.float32, (B, H))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().rf_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, L, D, 0 if nseg is None else int(nseg),
+                                         float(scale), RF_F32 if out.dtype == torch.float32 else RF_BF16, _ptr(out),
+                                         _ptr(lse), _stream(q)))
     return out, lse
 
 

@@ -5,9 +5,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -209,9 +211,49 @@ size_t rf_attn_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t D,
     return decode_ws_bytes(rows, D, nseg);
 }
 
-rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L, int64_t D,
-                         int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse, void* workspace,
-                         size_t ws_bytes, rf_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Device scratch of rf_attn_decode_noalloc: the segment partials live in this file-scope
+// array instead of a caller workspace. Host code never uses the array's name as an address
+// (on the host it is only a stand-in); the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and is kept per device.
+constexpr size_t kDecodeScratchBytes = RF_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The calling thread's current device's copy of `scratch`, or an error status.
+rf_status decode_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "rf_attn_decode_noalloc: hipGetDevice");
+    RF_REQUIRE(dev >= 0 && dev < kMaxDevices, RF_ERR_UNSUPPORTED, "device index %d is beyond the %d supported", dev,
+               kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return device_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                     "rf_attn_decode_noalloc: hipGetSymbolAddress(scratch)");
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RF_OK;
+}
+
+// The body shared by rf_attn_decode (caller workspace) and rf_attn_decode_noalloc (the
+// static scratch, use_scratch = true).
+rf_status attn_decode_impl(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L, int64_t D,
+                           int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse, void* workspace,
+                           size_t ws_bytes, bool use_scratch, rf_stream stream) {
     RF_PTR(q, "q");
     RF_PTR(k, "k");
     RF_PTR(v, "v");
@@ -246,6 +288,15 @@ rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B,
         return device_status(e, "rf_attn_decode launch");
     }
     const size_t need = decode_ws_bytes(rows, D, nseg);
+    if (use_scratch) {
+        RF_REQUIRE(need <= kDecodeScratchBytes, RF_ERR_UNSUPPORTED,
+                   "%lld rows x %lld segments need %zu bytes of partials, beyond the %zu-byte static scratch "
+                   "(use fewer segments, or rf_attn_decode with a workspace)",
+                   (long long)rows, (long long)nseg, need, kDecodeScratchBytes);
+        const rf_status st = decode_scratch(&workspace);
+        if (st != RF_OK) return st;
+        ws_bytes = kDecodeScratchBytes;
+    }
     RF_REQUIRE(ws_bytes >= need, RF_ERR_BUFFER_TOO_SMALL, "workspace too small: %zu bytes, need %zu", ws_bytes, need);
     RF_PTR(workspace, "workspace");
     const uint64_t n = uint64_t(rows) * uint64_t(nseg);
@@ -261,6 +312,22 @@ rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B,
                                            s);
     if (e == hipSuccess) e = rf::launch_segment_merge(pm, ps, po, rows, nseg, int(D), out_dt == RF_BF16, o, lse, s);
     return device_status(e, "rf_attn_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L, int64_t D,
+                         int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse, void* workspace,
+                         size_t ws_bytes, rf_stream stream) {
+    return attn_decode_impl(q, k, v, B, H, L, D, nseg, scale, out_dt, o, lse, workspace, ws_bytes, false, stream);
+}
+
+rf_status rf_attn_decode_noalloc(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L,
+                                 int64_t D, int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse,
+                                 rf_stream stream) {
+    return attn_decode_impl(q, k, v, B, H, L, D, nseg, scale, out_dt, o, lse, nullptr, 0, true, stream);
 }
 
 rf_status rf_mla_decode_split(const void* q, const void* kv, int64_t B, int64_t H, int64_t L, int64_t d_qk,

@@ -27,7 +27,8 @@
  *    call returns an error status, launches nothing and sets rf_last_error().
  *    A launch failure returns RF_ERR_DEVICE. Faults inside a kernel surface at
  *    the caller's next synchronisation, as for any HIP kernel.
- *  - Thread-safe: the only state is a thread-local error message.
+ *  - Thread-safe: the only state is a thread-local error message, plus the
+ *    per-device address of rf_attn_decode_noalloc's static scratch.
  *  - No call throws across the ABI or aborts the process.
  */
 #ifndef LIBRF_H
@@ -40,7 +41,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 2
+#define RF_ABI_VERSION 3
 
 /* Exported symbols (the library is built with hidden visibility by default). */
 #if defined(__GNUC__) || defined(__clang__)
@@ -212,6 +213,32 @@ RF_API size_t rf_attn_decode_workspace_size(int64_t B, int64_t H, int64_t L, int
 RF_API rf_status rf_attn_decode(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t L,
                                 int64_t D, int64_t nseg, float scale, rf_dtype out_dt, void* o, float* lse,
                                 void* workspace, size_t ws_bytes, rf_stream stream);
+
+/* Bytes of device scratch that rf_attn_decode_noalloc holds per GPU (32 MiB). */
+#define RF_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * rf_attn_decode_noalloc -- rf_attn_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and kernels as rf_attn_decode, without the workspace: the
+ * segment partials go to a static device array of RF_DECODE_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (its address is looked up
+ * once per device, on the first call made with that device current). The call allocates
+ * nothing and frees nothing.
+ *
+ *   Arguments as for rf_attn_decode, minus workspace and ws_bytes.
+ *   The partials need rf_attn_decode_workspace_size(B, H, L, D, nseg) bytes; a split whose
+ *   partials exceed RF_DECODE_SCRATCH_BYTES returns RF_ERR_UNSUPPORTED (one segment needs
+ *   no scratch at all).
+ *   Every call on one GPU shares that GPU's scratch (no initial contents are needed; it
+ *   keeps whatever the last call left): calls that may run concurrently on one GPU (on
+ *   different streams, or from different threads) race on it and must be serialised by
+ *   the caller.
+ */
+RF_API rf_status rf_attn_decode_noalloc(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                                        int64_t L, int64_t D, int64_t nseg, float scale, rf_dtype out_dt, void* o,
+                                        float* lse, rf_stream stream);
 
 /*
  * rf_mla_decode_split -- multi-head latent attention (MLA) decode, first kernel of two.

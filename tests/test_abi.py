@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
         "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split", "rf_row_cascade",
-        "rf_attn_decode_workspace_size", "rf_attn_decode",
+        "rf_attn_decode_workspace_size", "rf_attn_decode", "rf_attn_decode_noalloc",
         "rf_moe_route_workspace_size",
         "rf_moe_route",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rf_abi_version() == 2
+    assert lib.rf_abi_version() == 3
     for code, name in [(0, b"RF_OK"), (1, b"RF_ERR_INVALID_ARGUMENT"), (2, b"RF_ERR_UNSUPPORTED"),
                        (3, b"RF_ERR_BUFFER_TOO_SMALL"), (4, b"RF_ERR_DEVICE")]:
         assert lib.rf_status_string(code) == name
@@ -84,6 +84,10 @@ def test_decode_split_validation(lib):
     assert _split(lib, nseg=0) == INVALID
     assert _split(lib, nseg=65) == INVALID
     assert b"nseg" in lib.rf_last_error()
+    n = lib.rf_attn_decode_noalloc
+    assert n(P, P2, P3, 2, 4, 300, 96, 3, 0.08, 1, P4, None, None) == UNSUPPORTED        # D 96
+    assert n(P, P2, P3, 2, 4, 300, 128, 3, 0.08, 1, P, None, None) == INVALID           # o over q
+    assert n(P, P2, P3, 1 << 22, 1, 1024, 64, 1024, 0.1, 1, P4, None, None) == UNSUPPORTED
     assert _split(lib, L=0) == INVALID
     assert _split(lib, D=80) == UNSUPPORTED
     assert _split(lib, pm=P5) == INVALID                    # part_m aliases part_s
@@ -237,3 +241,7 @@ def test_decode_one_call_validation(lib):
     # 2^22 rows x 1024 segments: more split waves than the launch can index, refused on the host
     assert d(P, P2, P3, 1 << 22, 1, 1024, 64, 1024, 0.1, 1, P4, None, P5, 1 << 40, None) == UNSUPPORTED
     assert b"nseg" in lib.rf_last_error()
+    n = lib.rf_attn_decode_noalloc
+    assert n(P, P2, P3, 2, 4, 300, 96, 3, 0.08, 1, P4, None, None) == UNSUPPORTED        # D 96
+    assert n(P, P2, P3, 2, 4, 300, 128, 3, 0.08, 1, P, None, None) == INVALID           # o over q
+    assert n(P, P2, P3, 1 << 22, 1, 1024, 64, 1024, 0.1, 1, P4, None, None) == UNSUPPORTED
