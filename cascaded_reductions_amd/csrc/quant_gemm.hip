@@ -37,6 +37,7 @@ namespace {
 // ------------------------------------------------------------------ 1. per-row quantisation
 
 constexpr int QT = 256;   // threads per workgroup
+constexpr float kMinRecipSigma = 0x1p-60f;   // smallest row scale quantised through the reciprocal
 
 __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -47,10 +48,13 @@ __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d) {
 // The IEEE fp32 quotient x / sigma from the correctly rounded reciprocal r = 1 / sigma:
 // q0 = x r is within one ulp of x / sigma, the residual x - q0 sigma is exact in one
 // FMA, and q0 + residual * r rounded once is the correctly rounded quotient
-// (Markstein, IBM J. Res. Dev. 34(1), 1990). Overflow cannot occur (|q| <= 448) and an
-// underflowing quotient is far below the smallest E4M3FN subnormal, so its code (+-0)
-// does not depend on the last bits. The correction turns x = -0 into +0, so the sign
-// is restored from x (sigma > 0: the quotient always has the sign of x).
+// (Markstein, IBM J. Res. Dev. 34(1), 1990). Overflow cannot occur (|q| <= 448). The
+// residual is exact whenever x >= 2^-103; with sigma >= 2^-60 every x whose code can be
+// non-zero (x >= sigma 2^-10) is far above that, and a smaller x gives a quotient far
+// below the smallest E4M3FN subnormal, whose code (+-0) does not depend on the last
+// bits. (Rows with sigma < 2^-60, where 1 / sigma may even overflow, divide instead.)
+// The correction turns x = -0 into +0, so the sign is restored from x (sigma > 0: the
+// quotient always has the sign of x).
 __device__ __forceinline__ float div_rn(float x, float sigma, float r) {
     const float q0 = x * r;
     const float e = fmaf(-q0, sigma, x);
@@ -106,12 +110,21 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
 
     auto quant8 = [&](const u32x4& t, int ch) {
         uint32_t out0 = 0u, out1 = 0u;
-        if (sigma > 0.f) {
+        if (sigma >= kMinRecipSigma) {
             float q[8];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 q[2 * w] = div_rn(bf16_lo(t[w]), sigma, r);
                 q[2 * w + 1] = div_rn(bf16_hi(t[w]), sigma, r);
+            }
+            out0 = codes4(q[0], q[1], q[2], q[3]);
+            out1 = codes4(q[4], q[5], q[6], q[7]);
+        } else if (sigma > 0.f) {              // rows of tiny magnitude: IEEE division
+            float q[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                q[2 * w] = bf16_lo(t[w]) / sigma;
+                q[2 * w + 1] = bf16_hi(t[w]) / sigma;
             }
             out0 = codes4(q[0], q[1], q[2], q[3]);
             out1 = codes4(q[4], q[5], q[6], q[7]);

@@ -65,6 +65,21 @@ def test_zero_and_tiny_rows(rf):
     assert np.all(y[3] == 0)
 
 
+def test_extreme_row_magnitudes(rf):
+    """Rows whose absolute maximum spans bf16's range: a bf16 subnormal absmax (the scale is an
+    fp32 subnormal and its reciprocal would overflow), scales on both sides of the switch
+    from reciprocal-and-correction to division at 2^-60, and large magnitudes. Codes and
+    scales bit-exact."""
+    x, wq, ws = quant_inputs(24, 64, 256, seed=74)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    scales = [2.0 ** -140, 2.0 ** -133, 2.0 ** -128, 2.0 ** -120, 2.0 ** -100, 2.0 ** -62, 2.0 ** -59,
+              2.0 ** -52, 2.0 ** -49, 2.0 ** 20, 2.0 ** 60, 2.0 ** 90]
+    for i, sc in enumerate(scales):
+        xf[i] = xf[i] * sc
+    x = f32_to_bf16_bits(xf.astype(np.float32))
+    _check(rf, x, wq, ws)
+
+
 def test_workspace_path_matches(rf):
     x, wq, ws = quant_inputs(130, 200, 512, seed=72)
     a = _check(rf, x, wq, ws, use_workspace=False)
