@@ -16,7 +16,7 @@ __all__ = [
     "RFError", "load", "lib_path", "RF_F32", "RF_BF16", "RF_ATTN_AUTO", "RF_ATTN_INCREMENTAL", "RF_ATTN_WHOLE_ROW",
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_noalloc",
     "attn_decode_segments",
-    "mla_decode_split", "mla_decode", "row_cascade",
+    "mla_decode_split", "mla_decode", "row_cascade", "cascade_gemm",
     "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
@@ -55,6 +55,7 @@ _SIGS = {
     "rf_attn_decode_noalloc": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _c.c_int, _P, _P, _P], _c.c_int),
     "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_row_cascade": ([_c.c_int, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
+    "rf_cascade_gemm": ([_c.c_int, _P, _P, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
     "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -332,6 +333,28 @@ def row_cascade(kind: str, x, payload=None, k: int = 0):
     _check(load().rf_row_cascade(_CASCADES[kind], _ptr(x), _ptr(payload) if P else None, R, N, P, k, _ptr(out),
                                  _ptr(idx), _stream(x)))
     return (out, idx) if idx is not None else out
+
+
+_CASCADE_GEMMS = {"softmax": 0, "absmax": 1}
+
+
+def cascade_gemm(kind: str, x, w, *, y=None, stat=None):
+    """A row-scaled GEMM cascade from the template: x [M, K] fp32, w [K, N] bf16 ->
+    (y [M, N] fp32, stat [M] fp32). kind "softmax": y = softmax(x) w, stat = logsumexp(x);
+    "absmax": y = (x / max|x|) w, stat = max|x|."""
+    torch = _torch()
+    if kind not in _CASCADE_GEMMS:
+        raise ValueError(f"kind must be one of {sorted(_CASCADE_GEMMS)}")
+    M, K = x.shape
+    N = w.shape[1]
+    _need(x, "x", torch.float32, (M, K))
+    _need(w, "w", torch.bfloat16, (K, N))
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device) if y is None else y
+    stat = torch.empty((M,), dtype=torch.float32, device=x.device) if stat is None else stat
+    _need(y, "y", torch.float32, (M, N))
+    _need(stat, "stat", torch.float32, (M,))
+    _check(load().rf_cascade_gemm(_CASCADE_GEMMS[kind], _ptr(x), _ptr(w), M, K, N, _ptr(y), _ptr(stat), _stream(x)))
+    return y, stat
 
 
 # ------------------------------------------------------------------ MoE gate

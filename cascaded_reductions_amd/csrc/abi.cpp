@@ -396,6 +396,29 @@ rf_status rf_row_cascade(rf_cascade kind, const float* x, const float* payload, 
     return device_status(e, "rf_row_cascade launch");
 }
 
+rf_status rf_cascade_gemm(rf_cascade_gemm_kind kind, const float* x, const void* w, int64_t M, int64_t K, int64_t N,
+                          float* y, float* stat, rf_stream stream) {
+    RF_REQUIRE(kind == RF_CASCADE_GEMM_SOFTMAX || kind == RF_CASCADE_GEMM_ABSMAX, RF_ERR_INVALID_ARGUMENT,
+               "unknown cascade GEMM kind %d", int(kind));
+    RF_PTR(x, "x");
+    RF_PTR(w, "w");
+    RF_PTR(y, "y");
+    RF_OPT_PTR(stat, "stat");
+    RF_REQUIRE(M >= 1 && K >= 1 && N >= 1, RF_ERR_INVALID_ARGUMENT, "M, K and N must be >= 1");
+    RF_REQUIRE(N == 64 || N == 128, RF_ERR_UNSUPPORTED, "N must be 64 or 128 (got %lld)", (long long)N);
+    RF_REQUIRE(K % 4 == 0 && K < (int64_t(1) << 24), RF_ERR_UNSUPPORTED,
+               "K must be a multiple of 4 below 2^24 (got %lld)", (long long)K);
+    int64_t nx, nw, ny;
+    RF_REQUIRE(prod({M, K}, &nx) && nx < kMaxElems && prod({K, N}, &nw) && prod({M, N}, &ny) && ny < kMaxElems,
+               RF_ERR_UNSUPPORTED, "problem too large");
+    RF_REQUIRE(!overlap(y, ny * 4, x, nx * 4) && !overlap(y, ny * 4, w, nw * 2) && !overlap(stat, M * 4, x, nx * 4) &&
+                   !overlap(stat, M * 4, w, nw * 2) && !overlap(stat, M * 4, y, ny * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    const hipError_t e = rf::launch_cascade_gemm(int(kind), x, static_cast<const uint16_t*>(w), M, K, int(N), y, stat,
+                                                 static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_cascade_gemm launch");
+}
+
 int64_t rf_attn_decode_segments(int64_t rows, int64_t L, int64_t num_cus) {
     if (rows < 1 || L < 1) {
         fail(RF_ERR_INVALID_ARGUMENT, "rows and L must be >= 1 (got %lld, %lld)", (long long)rows, (long long)L);

@@ -53,6 +53,11 @@ hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T
                             int E, int k, int32_t* idx, float* w, float* scores, void* workspace,
                             hipStream_t stream);
 
+// Row-scaled GEMM cascades from the generic template: kind 0 y = softmax(x) w with stat = lse,
+// kind 1 y = (x / max|x|) w with stat = max|x|; x [M, K] fp32, w [K, N] bf16, y [M, N] fp32.
+hipError_t launch_cascade_gemm(int kind, const float* x, const uint16_t* w, int64_t M, int64_t K, int N, float* y,
+                               float* stat, hipStream_t stream);
+
 // Per-row dynamic E4M3FN quantisation of x [M, K] bf16 -> codes [M, K], scale [M].
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* codes,
                              float* x_scale, hipStream_t stream);

@@ -1,4 +1,4 @@
-// Row cascades built from the generic incremental template (cascade.hpp).
+// Row cascades built from the generic incremental template (cascade.hpp: Cascade<Spec>).
 //
 // A group of G lanes folds one row of x [R, N] (fp32; G from 4 to 64 so that every lane
 // absorbs at least 32 elements): lane i absorbs elements 4i .. 4i+3 of every 4G-element
@@ -25,21 +25,22 @@ using namespace cascade;
 // state, streaming 16-byte loads in flight when there is no payload), then the group's
 // states are merged by xor shuffles within the group, in a fixed order.
 template <class Spec, int G>
-__device__ __forceinline__ typename Spec::State fold_row(const float* __restrict__ xr, const float* __restrict__ pr,
-                                                         int64_t N, int li) {
-    constexpr int P = Spec::kPayload;
+__device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* __restrict__ xr,
+                                                                  const float* __restrict__ pr, int64_t N, int li) {
+    using C = Cascade<Spec>;
+    constexpr int P = C::kPayload;
     constexpr int STRIDE = 4 * G;
-    typename Spec::State st = Spec::identity();
+    typename C::State st = C::identity();
     auto absorb4 = [&](const float4& v, int64_t j0) {
         const float xs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Spec::absorb(st, xs[e], int32_t(j0 + e), P ? pr + (j0 + e) * P : nullptr);
+        for (int e = 0; e < 4; ++e) C::absorb(st, xs[e], int32_t(j0 + e), P ? pr + (j0 + e) * P : nullptr);
     };
     const bool vec = (N & 3) == 0;            // 16-byte loads need aligned rows
     // Eight loads in flight when only x is read (nontemporal: the row is read once), four for
     // a large state (top-k: its registers would cost occupancy); with a payload its loads
     // already overlap.
-    constexpr int UN = sizeof(typename Spec::State) > 32 ? 4 : 8;
+    constexpr int UN = sizeof(typename C::State) > 32 ? 4 : 8;
     const int64_t full4 = vec && P == 0 ? N / (UN * STRIDE) * (UN * STRIDE) : 0;
     int64_t j0 = 4 * li;
     for (; j0 < full4; j0 += UN * STRIDE) {
@@ -80,14 +81,14 @@ __device__ __forceinline__ typename Spec::State fold_row(const float* __restrict
             for (int u = 0; u < UPW; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    Spec::absorb(st, xv[u][e], int32_t(j0 + u * STRIDE + e), &pv[u][e * P]);
+                    C::absorb(st, xv[u][e], int32_t(j0 + u * STRIDE + e), &pv[u][e * P]);
         }
     }
     const int64_t full = vec ? N / STRIDE * STRIDE : 0;
     for (; j0 < full; j0 += STRIDE) absorb4(*reinterpret_cast<const float4*>(xr + j0), j0);
-    for (int64_t j = full + li; j < N; j += G) Spec::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
+    for (int64_t j = full + li; j < N; j += G) C::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
 #pragma unroll
-    for (int mask = G / 2; mask >= 1; mask >>= 1) st = Spec::combine(st, shfl_xor_state(st, mask));
+    for (int mask = G / 2; mask >= 1; mask >>= 1) st = C::combine(st, shfl_xor_state(st, mask));
     return st;
 }
 
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void lse_kernel(const float* __restrict__ x, i
     const int64_t r = row_of<G>(li);
     if (r >= R) return;
     const auto st = fold_row<LogSumExp, G>(x + r * N, nullptr, N, li);
-    if (li == 0) out[r] = st.m + __logf(st.s);
+    if (li == 0) out[r] = st.lead + __logf(st.acc.s);
 }
 
 template <int G, int P>
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(256) void softmax_weighted_kernel(const float* __re
     const auto st = fold_row<SoftmaxWeighted<P>, G>(x + r * N, payload + r * N * P, N, li);
     for (int i0 = 0; i0 < P; i0 += G) {
         const int i = i0 + li;
-        float o = st.o[0];
+        float o = st.acc.o[0];
 #pragma unroll
-        for (int c = 1; c < P; ++c) o = i == c ? st.o[c] : o;
-        if (i < P) out[r * P + i] = o / st.s;
+        for (int c = 1; c < P; ++c) o = i == c ? st.acc.o[c] : o;
+        if (i < P) out[r * P + i] = o / st.acc.s;
     }
 }
 
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
         float e[K], den = 0.f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            e[i] = i < k ? __expf(st.s[i] - st.s[0]) : 0.f;
+            e[i] = i < k ? __expf(st.lead.s[i] - st.lead.s[0]) : 0.f;
             den += e[i];
         }
         const float inv = 1.f / den;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
         for (int i = 0; i < K; ++i)
             if (i < k) {
                 out[r * k + i] = e[i] * inv;
-                out_idx[r * k + i] = st.i[i];
+                out_idx[r * k + i] = st.lead.i[i];
             }
     }
 }
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(256) void mean_var_kernel(const float* __restrict__
     if (r >= R) return;
     const auto st = fold_row<MeanVar, G>(x + r * N, nullptr, N, li);
     if (li == 0) {
-        out[r * 2] = st.mean;
-        out[r * 2 + 1] = st.m2 / float(st.n);
+        out[r * 2] = st.lead.mean;
+        out[r * 2 + 1] = st.acc.m2 / float(st.lead.n);
     }
 }
 

@@ -307,6 +307,37 @@ typedef enum rf_cascade {
 RF_API rf_status rf_row_cascade(rf_cascade kind, const float* x, const float* payload, int64_t R, int64_t N,
                                 int64_t P, int64_t k, float* out, int32_t* out_idx, rf_stream stream);
 
+/* The row-scaled GEMM cascades rf_cascade_gemm instantiates from the same template. */
+typedef enum rf_cascade_gemm_kind {
+    RF_CASCADE_GEMM_SOFTMAX = 0, /* y = softmax(x) w,        stat = ln sum_k exp(x_k)  */
+    RF_CASCADE_GEMM_ABSMAX = 1   /* y = (x / max|x|) w,      stat = max_k |x_k|        */
+} rf_cascade_gemm_kind;
+
+/*
+ * rf_cascade_gemm -- a row-scaled GEMM cascade on the matrix cores, from the generic template.
+ *
+ * For every row x of X, a cascade whose leading reduction scales the row and whose last
+ * reduction is a contraction with the weight W (technical summary, Methodologie 1-2; the
+ * explainer's sections 2.2-2.3):
+ *   RF_CASCADE_GEMM_SOFTMAX  d1 = max_k x_k, d2 = sum_k exp(x_k - d1),
+ *                            y = sum_k exp(x_k - d1) W[k, :] / d2, stat = d1 + ln d2
+ *                            (the softmax -> GEMM cascade of section 4.1 with the scores
+ *                            given; -inf entries are masked; a row must have a finite entry);
+ *   RF_CASCADE_GEMM_ABSMAX   d1 = max_k |x_k|, y = sum_k (x_k / d1) W[k, :], stat = d1
+ *                            (the row scaling of section 4.3's quantisation cascade, without
+ *                            the rounding; a zero row gives y = 0 and stat = 0).
+ * The template keeps the lead, corrects the running output by H(d_new) H^-1(d_old) when it
+ * moves (exp(d1_old - d1_new), or d1_old / d1_new), and forms the contraction on the bf16
+ * matrix cores with fp32 accumulation, each per-element weight split into a bf16 head and
+ * a bf16 tail (about 2^-17 relative; the softmax's sum reads the same two parts).
+ *
+ *   x     [M, K] fp32.   w  [K, N] bf16 (N contiguous).   y  [M, N] fp32.
+ *   stat  [M] fp32, may be NULL.
+ *   Supported: M >= 1; 4 <= K < 2^24 and K % 4 == 0; N in {64, 128}; M*K below 2^40.
+ */
+RF_API rf_status rf_cascade_gemm(rf_cascade_gemm_kind kind, const float* x, const void* w, int64_t M, int64_t K,
+                                 int64_t N, float* y, float* stat, rf_stream stream);
+
 /*
  * rf_moe_route_workspace_size -- bytes of device workspace rf_moe_route needs.
  */

@@ -9,7 +9,14 @@ reductions where each one uses the results of the previous ones), in float64:
 * topk_softmax:     the k best (score descending, index ascending), then the
                     softmax over those k (oracle.moe.topk_softmax);
 * mean_var:         mu = mean_j x_j, then var = sum_j (x_j - mu)^2 / N
-                    (population variance, the second reduction uses the first).
+                    (population variance, the second reduction uses the first);
+* softmax_gemm:     the softmax -> GEMM cascade with the scores given: per row of
+                    x [M, K], m = max_k x_k, s = sum_k exp(x_k - m), then
+                    y = sum_k exp(x_k - m) w_k / s against w [K, N], lse = m + ln s
+                    ([explainer] sections 2.1 and 4.1);
+* absmax_gemm:      a row-scaled GEMM: a = max_k |x_k|, then y = sum_k (x_k / a) w_k
+                    (the dynamic-quant cascade of [explainer] section 4.3 without the
+                    rounding); a row of zeros gives a = 0 and y = 0.
 """
 from __future__ import annotations
 
@@ -42,4 +49,24 @@ def mean_var(x):
     return np.concatenate([mu, var], axis=1)
 
 
-__all__ = ["logsumexp", "softmax_weighted", "topk_softmax", "mean_var"]
+def softmax_gemm(x, w):
+    """x [M, K] (scores; -inf entries are masked), w [K, N] -> (y [M, N], lse [M])."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    m = x.max(axis=1, keepdims=True)                 # reduction 1: the row maximum
+    e = np.exp(x - m)
+    s = e.sum(axis=1, keepdims=True)                 # reduction 2: uses reduction 1
+    y = (e @ w) / s                                  # reduction 3: uses reductions 1 and 2
+    return y, (m + np.log(s))[:, 0]
+
+
+def absmax_gemm(x, w):
+    """x [M, K], w [K, N] -> (y [M, N], a [M]) with a the row's absolute maximum."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    a = np.abs(x).max(axis=1)                        # reduction 1: the row's absolute maximum
+    scaled = x / np.where(a == 0, 1.0, a)[:, None]   # a zero row stays zero
+    return scaled @ w, a                             # reduction 2: uses reduction 1
+
+
+__all__ = ["logsumexp", "softmax_weighted", "topk_softmax", "mean_var", "softmax_gemm", "absmax_gemm"]

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "rf_abi_version", "rf_status_string", "rf_last_error", "rf_softmax_gemm_fused", "rf_softmax_gemm_fused_mode",
         "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split", "rf_row_cascade",
+        "rf_cascade_gemm",
         "rf_attn_decode_workspace_size", "rf_attn_decode", "rf_attn_decode_noalloc",
         "rf_moe_route_workspace_size",
         "rf_moe_route",
@@ -245,3 +246,16 @@ def test_decode_one_call_validation(lib):
     assert n(P, P2, P3, 2, 4, 300, 96, 3, 0.08, 1, P4, None, None) == UNSUPPORTED        # D 96
     assert n(P, P2, P3, 2, 4, 300, 128, 3, 0.08, 1, P, None, None) == INVALID           # o over q
     assert n(P, P2, P3, 1 << 22, 1, 1024, 64, 1024, 0.1, 1, P4, None, None) == UNSUPPORTED
+
+
+def test_cascade_gemm_validation(lib):
+    c = lib.rf_cascade_gemm
+    assert c(2, P, P2, 8, 64, 64, P3, None, None) == INVALID                    # unknown kind
+    assert c(0, None, P2, 8, 64, 64, P3, None, None) == INVALID                 # x NULL
+    assert c(0, P, P2, 0, 64, 64, P3, None, None) == INVALID                    # M = 0
+    assert c(0, P, P2, 8, 64, 96, P3, None, None) == UNSUPPORTED                # N = 96
+    assert c(1, P, P2, 8, 66, 64, P3, None, None) == UNSUPPORTED                # K % 4
+    assert c(1, P, P2, 8, 1 << 24, 64, P3 * 1000, None, None) == UNSUPPORTED    # K too long
+    assert c(0, P, P2, 8, 64, 64, P, None, None) == INVALID                     # y over x
+    assert c(0, P, P2, 8, 64, 64, P3, P3 + 16, None) == INVALID                 # stat over y
+    assert c(0, P + 8, P2, 8, 64, 64, P3, None, None) == INVALID                # misaligned x
