@@ -17,11 +17,11 @@ __all__ = [
     "softmax_gemm_fused", "attn_decode_split", "segment_merge", "attn_decode", "attn_decode_noalloc",
     "attn_decode_segments",
     "mla_decode_split", "mla_decode", "row_cascade", "cascade_gemm",
-    "moe_route", "moe_route_workspace_size", "quant_gemm", "quant_gemm_workspace_size",
+    "moe_route", "moe_route_split", "quant_gemm", "quant_gemm_workspace_size",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 3
+ABI_VERSION = 4
 RF_F32, RF_BF16 = 0, 1
 _STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARGUMENT", 2: "RF_ERR_UNSUPPORTED",
            3: "RF_ERR_BUFFER_TOO_SMALL", 4: "RF_ERR_DEVICE"}
@@ -56,8 +56,9 @@ _SIGS = {
     "rf_mla_decode_split": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P, _P, _P], _c.c_int),
     "rf_row_cascade": ([_c.c_int, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
     "rf_cascade_gemm": ([_c.c_int, _P, _P, _I64, _I64, _I64, _P, _P, _P], _c.c_int),
-    "rf_moe_route_workspace_size": ([_I64, _I64, _I64], _SZ),
-    "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
+    "rf_moe_route": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
+    "rf_moe_route_split_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "rf_moe_route_split": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_quant_gemm": ([_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
 }
@@ -360,15 +361,7 @@ def cascade_gemm(kind: str, x, w, *, y=None, stat=None):
 # ------------------------------------------------------------------ MoE gate
 
 
-def moe_route_workspace_size(T: int, Hd: int, E: int) -> int:
-    return int(load().rf_moe_route_workspace_size(T, Hd, E))
-
-
-def _moe_workspace(device, nbytes):
-    return _workspace("moe", device, nbytes)
-
-
-def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False, workspace=None):
+def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False):
     """x [T,Hd] bf16, w_gate [Hd,E] bf16 -> (idx [T,k] int32, w [T,k] fp32, scores [T,E] fp32 or None)."""
     torch = _torch()
     T, Hd = x.shape
@@ -383,12 +376,30 @@ def moe_route(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores
         scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
     if scores is not None:
         _need(scores, "scores", torch.float32, (T, E))
-    need = moe_route_workspace_size(T, Hd, E)
-    if workspace is None:
-        workspace = _moe_workspace(x.device, need)
-    _need(workspace, "workspace", torch.uint8)
-    _check(load().rf_moe_route(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores),
-                               _ptr(workspace), workspace.numel(), _stream(x)))
+    _check(load().rf_moe_route(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores), _stream(x)))
+    return idx, w, scores
+
+
+def moe_route_split(x, w_gate, k: int, *, idx=None, w=None, scores=None, return_scores: bool = False):
+    """rf_moe_route_split: the two-launch form over a split hidden axis (scratch cached per
+    device and stream). Same arguments and results as moe_route."""
+    torch = _torch()
+    T, Hd = x.shape
+    E = w_gate.shape[1]
+    _need(x, "x", torch.bfloat16)
+    _need(w_gate, "w_gate", torch.bfloat16, (Hd, E))
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if w is None else w
+    _need(idx, "idx", torch.int32, (T, k))
+    _need(w, "w", torch.float32, (T, k))
+    if scores is None and return_scores:
+        scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, (T, E))
+    need = int(load().rf_moe_route_split_workspace_size(T, Hd, E))
+    ws = _workspace("moe_split", x.device, need)
+    _check(load().rf_moe_route_split(_ptr(x), _ptr(w_gate), T, Hd, E, k, _ptr(idx), _ptr(w), _ptr(scores), _ptr(ws),
+                                     ws.numel(), _stream(x)))
     return idx, w, scores
 
 

@@ -472,45 +472,72 @@ rf_status rf_segment_merge(const float* part_m, const float* part_s, const float
     return device_status(e, "rf_segment_merge launch");
 }
 
-size_t rf_moe_route_workspace_size(int64_t T, int64_t Hd, int64_t E) {
-    if (T < 1 || Hd < 1 || E < 1 || T > INT32_MAX || Hd > INT32_MAX || E > 256) return 0;
-    return rf::moe_workspace_bytes(T, Hd, E);
-}
+}  // extern "C"
 
-rf_status rf_moe_route(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E,
-                       int64_t k, int32_t* idx, float* w, float* scores, void* workspace,
-                       size_t ws_bytes, rf_stream stream) {
+namespace {
+// Arguments shared by both forms of the MoE gate; RF_OK when they are valid.
+rf_status moe_check(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E, int64_t k, int32_t* idx,
+                    float* w, float* scores) {
     RF_PTR(x, "x");
     RF_PTR(w_gate, "w_gate");
     RF_PTR(idx, "idx");
     RF_PTR(w, "w");
     RF_OPT_PTR(scores, "scores");
-    RF_OPT_PTR(workspace, "workspace");
     RF_REQUIRE(T >= 1 && Hd >= 1 && E >= 1, RF_ERR_INVALID_ARGUMENT, "T, Hd and E must be >= 1");
     RF_REQUIRE(k >= 1 && k <= E, RF_ERR_INVALID_ARGUMENT, "need 1 <= k <= E (k=%lld, E=%lld)", (long long)k,
                (long long)E);
     RF_REQUIRE(Hd % 32 == 0, RF_ERR_UNSUPPORTED, "Hd must be a multiple of 32 (got %lld)", (long long)Hd);
+    RF_REQUIRE(Hd < (int64_t(1) << 26), RF_ERR_UNSUPPORTED, "Hd must be below 2^26 (got %lld)", (long long)Hd);
     RF_REQUIRE(E >= 16 && E <= 256 && E % 16 == 0, RF_ERR_UNSUPPORTED,
                "E must be a multiple of 16 in [16, 256] (got %lld)", (long long)E);
     RF_REQUIRE(k <= 8, RF_ERR_UNSUPPORTED, "k must be <= 8 (got %lld)", (long long)k);
     int64_t nx, ns;
-    RF_REQUIRE(prod({T, Hd}, &nx) && nx < kMaxElems && prod({T, E}, &ns) && T <= INT32_MAX && Hd <= INT32_MAX,
+    RF_REQUIRE(prod({T, Hd}, &nx) && nx < kMaxElems && prod({T, E}, &ns) && T <= INT32_MAX,
                RF_ERR_UNSUPPORTED, "tensor too large");
-    const size_t need = rf_moe_route_workspace_size(T, Hd, E);
-    RF_REQUIRE(workspace != nullptr && ws_bytes >= need, RF_ERR_BUFFER_TOO_SMALL,
-               "workspace of %zu bytes needed (got %zu)", need, workspace ? ws_bytes : size_t(0));
     RF_REQUIRE(!overlap(idx, T * k * 4, x, nx * 2) && !overlap(idx, T * k * 4, w_gate, Hd * E * 2) &&
                    !overlap(w, T * k * 4, x, nx * 2) && !overlap(w, T * k * 4, w_gate, Hd * E * 2) &&
                    !overlap(idx, T * k * 4, w, T * k * 4) && !overlap(scores, ns * 4, x, nx * 2) &&
                    !overlap(scores, ns * 4, w_gate, Hd * E * 2) && !overlap(scores, ns * 4, idx, T * k * 4) &&
-                   !overlap(scores, ns * 4, w, T * k * 4) && !overlap(workspace, need, x, nx * 2) &&
-                   !overlap(workspace, need, w_gate, Hd * E * 2) && !overlap(workspace, need, idx, T * k * 4) &&
-                   !overlap(workspace, need, w, T * k * 4) && !overlap(workspace, need, scores, ns * 4),
-               RF_ERR_INVALID_ARGUMENT, "outputs and workspace must not alias inputs or each other");
-    hipError_t e = rf::launch_moe_route(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate), T,
-                                        Hd, int(E), int(k), idx, w, scores, workspace,
-                                        static_cast<hipStream_t>(stream));
+                   !overlap(scores, ns * 4, w, T * k * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    return RF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+rf_status rf_moe_route(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E, int64_t k, int32_t* idx,
+                       float* w, float* scores, rf_stream stream) {
+    const rf_status st = moe_check(x, w_gate, T, Hd, E, k, idx, w, scores);
+    if (st != RF_OK) return st;
+    const hipError_t e = rf::launch_moe_route(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
+                                              T, Hd, int(E), int(k), idx, w, scores, static_cast<hipStream_t>(stream));
     return device_status(e, "rf_moe_route launch");
+}
+
+size_t rf_moe_route_split_workspace_size(int64_t T, int64_t Hd, int64_t E) {
+    if (T < 1 || Hd < 1 || E < 1 || T > INT32_MAX || Hd > INT32_MAX || E > 256) return 0;
+    return rf::moe_split_workspace_bytes(T, Hd, E);
+}
+
+rf_status rf_moe_route_split(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E, int64_t k,
+                             int32_t* idx, float* w, float* scores, void* workspace, size_t ws_bytes,
+                             rf_stream stream) {
+    const rf_status st = moe_check(x, w_gate, T, Hd, E, k, idx, w, scores);
+    if (st != RF_OK) return st;
+    RF_OPT_PTR(workspace, "workspace");
+    const size_t need = rf_moe_route_split_workspace_size(T, Hd, E);
+    RF_REQUIRE(workspace != nullptr && ws_bytes >= need, RF_ERR_BUFFER_TOO_SMALL,
+               "workspace of %zu bytes needed (got %zu)", need, workspace ? ws_bytes : size_t(0));
+    const uint64_t nx = uint64_t(T) * uint64_t(Hd), ns = uint64_t(T) * uint64_t(E);
+    RF_REQUIRE(!overlap(workspace, need, x, nx * 2) && !overlap(workspace, need, w_gate, Hd * E * 2) &&
+                   !overlap(workspace, need, idx, T * k * 4) && !overlap(workspace, need, w, T * k * 4) &&
+                   !overlap(workspace, need, scores, ns * 4),
+               RF_ERR_INVALID_ARGUMENT, "the workspace must not alias the tensors");
+    const hipError_t e = rf::launch_moe_route_split(static_cast<const uint16_t*>(x),
+                                                    static_cast<const uint16_t*>(w_gate), T, Hd, int(E), int(k), idx,
+                                                    w, scores, workspace, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_moe_route_split launch");
 }
 
 size_t rf_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {

@@ -95,9 +95,23 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base
 }
 
 // The same with a wave-uniform 64-bit global base (SGPR pair) and a per-lane 32-bit
-// byte offset: the address costs no vector instruction.
+// byte offset: the address costs no vector instruction. A vector-memory instruction that
+// reads an SGPR written by a vector instruction (v_readfirstlane_b32, which the compiler
+// uses when it forms the base in VGPRs) needs 5 wait states, and the compiler's hazard
+// check does not see the operands of inline assembly, so the wait states are part of it.
 __device__ __forceinline__ void lds_dma16_sb(const void* gbase, uint32_t voff_bytes, uint32_t lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff_bytes), "s"(gbase), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff_bytes), "s"(gbase), "{m0}"(lds_base)
+                 : "memory");
+}
+
+// A pointer the caller knows to be wave-uniform, moved to scalar registers (the direct-load
+// helper above takes its global base in an SGPR pair).
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const T*>((uint64_t(hi) << 32) | lo);
 }
 
 // LDS byte address of a __shared__ object (wave-uniform when the pointer is).

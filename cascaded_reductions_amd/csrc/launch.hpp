@@ -46,12 +46,14 @@ hipError_t launch_segment_merge(const float* part_m, const float* part_s, const 
                                 int64_t rows, int64_t nseg, int D, bool out_bf16, void* o,
                                 float* lse, hipStream_t stream);
 
-// MoE gate: x [T, Hd] bf16, w [Hd, E] bf16 -> idx/w [T, k], optional scores [T, E].
-// The workspace holds the partial score blocks of the hidden ranges.
-size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E);
+// MoE gate in one launch: x [T, Hd] bf16, w [Hd, E] bf16 -> idx/w [T, k], optional scores [T, E].
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd,
-                            int E, int k, int32_t* idx, float* w, float* scores, void* workspace,
-                            hipStream_t stream);
+                            int E, int k, int32_t* idx, float* w, float* scores, hipStream_t stream);
+// The same in two launches over a split hidden axis; the workspace holds the partial score
+// blocks of the hidden ranges.
+size_t moe_split_workspace_bytes(int64_t T, int64_t Hd, int64_t E);
+hipError_t launch_moe_route_split(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd, int E, int k,
+                                  int32_t* idx, float* w, float* scores, void* workspace, hipStream_t stream);
 
 // Row-scaled GEMM cascades from the generic template: kind 0 y = softmax(x) w with stat = lse,
 // kind 1 y = (x / max|x|) w with stat = max|x|; x [M, K] fp32, w [K, N] bf16, y [M, N] fp32.

@@ -1,31 +1,24 @@
-// Fused MoE gate: scores = X W_gate -> top-k -> softmax over the k selected.
+// Fused MoE gate in one kernel: scores = X W_gate -> top-k -> softmax over the k selected.
 //
-// The cascade of the explainer "RedFuser框架：AI加速器中的算子融合技术解析",
-// section 4.2; the full score matrix is never written (except as an optional
-// debug output).
+// The cascade of the explainer "RedFuser框架：AI加速器中的算子融合技术解析", section 4.2,
+// as a single kernel that never stores the score matrix (only the optional debug copy
+// is written). Experts are ranked by (score descending, index ascending).
 //
-// The gate GEMM reads X once (16.8 MB at 2048 x 4096) but every token needs the
-// whole W_gate, so a kernel that gives each workgroup a few tokens and all of
-// the hidden axis would stream W through every CU. Instead the hidden axis is
-// split into ranges (the Multi-Segment idea of the technical summary
-// "RedFuser: An Automatic Operator Fusion Framework for Cascaded Reductions on
-// AI Accelerators", Methodologie 3, applied to the GEMM's sum):
-//  * workgroup (token block b, range r) stages W[range r] once in LDS, streams
-//    its 64 tokens' X[range r] straight into bf16 MFMA operands
-//    (v_mfma_f32_16x16x32_bf16; W enters through the transposing LDS read, so
-//    the [Hd, E] layout needs no transpose in memory), and writes a 64 x E
-//    partial score block to the workspace;
-//  * a second launch adds each token's range partials in range order -- a fixed
-//    order, so results are deterministic -- and runs the top-k and the softmax
-//    in registers: sixteen lanes per token each keep a sorted top-k list over a
-//    sixteenth of the experts, merged with four cross-lane steps. (Publishing the
-//    partials inside one launch would need an agent-scope release per
-//    workgroup, which on gfx950 writes back the whole L2 of the XCD; the
-//    kernel boundary orders the two phases instead -- the explainer's
-//    multi-kernel level, section 3.3.)
-// Experts are ranked by (score descending, index ascending).
-#include <type_traits>
-
+// Each workgroup owns TB = 8 tokens and all E experts, so no workgroup depends on
+// another (no partial scores leave the chip and no second launch is needed):
+//  * its 4 waves split the hidden axis into contiguous quarters and stream their quarter
+//    of W_gate ([32 hidden x E] bf16 chunks) and of the 8 tokens' X through wave-private
+//    LDS rings filled by direct global-to-LDS loads, 6 chunks ahead, so every wave runs
+//    without barriers until the end;
+//  * the gate GEMM runs on v_mfma_f32_16x16x32_bf16 with the tokens as the M dimension
+//    (8 of 16 rows used) and W entering through the transposing LDS read, so the [Hd, E]
+//    layout needs no transpose in memory;
+//  * the 4 waves' partial scores are added through LDS in a fixed order (deterministic),
+//    then sixteen lanes per token keep sorted top-k lists over a sixteenth of the experts,
+//    merged by four cross-lane steps, and the first lane applies the softmax over the k.
+// Every workgroup reads the whole W_gate (E * Hd * 2 bytes, 0.5 MiB at 4096 x 64) from its
+// XCD's L2 and X once; the per-CU rate of those L2 reads bounds the kernel (the two-launch
+// form in moe_route_split.hip reads a range of W per CU instead, and exchanges partials).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,27 +28,9 @@ namespace {
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int TBM = 64;               // tokens per token block
-constexpr int kLdsElems = 32768;      // W slice capacity (bf16 elements, 64 KiB)
-
-struct MoeGeom {
-    int64_t ntb, nranges;
-    int hr;
-    size_t part_bytes;
-};
-
-// Width of the hidden range one workgroup reduces: as wide as the 64 KiB LDS slice
-// allows, at most 512 (16 MFMA K-chunks of 32).
-constexpr int range_width(int E) { return (kLdsElems / E) / 32 * 32 < 512 ? (kLdsElems / E) / 32 * 32 : 512; }
-
-MoeGeom moe_geom(int64_t T, int64_t Hd, int64_t E) {
-    MoeGeom g;
-    g.ntb = ceil_div(T, TBM);
-    g.hr = range_width(int(E));
-    g.nranges = ceil_div(Hd, g.hr);
-    g.part_bytes = size_t(g.ntb * g.nranges * TBM * E * 4);
-    return g;
-}
+constexpr int TB = 8;                 // tokens per workgroup
+constexpr int NWAVE = 4;
+constexpr int WAVE_LDS = 36 * 1024;   // LDS ring bytes per wave
 
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
@@ -82,136 +57,153 @@ __device__ __forceinline__ void topk_insert(float (&ts)[K], int (&ti)[K], float 
     }
 }
 
-// Phase 1: partial scores of 64 tokens over one hidden range.
+// Ring geometry for E experts: a W chunk is 32 hidden rows x E bf16 (E / 16 KiB), an X
+// chunk pair is the 8 tokens x 64 hidden values (1 KiB). DEPTH chunk slots per wave.
 template <int NEB>
-__global__ __launch_bounds__(256) void moe_partial_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ wg, int64_t T,
-                                                          int64_t Hd, int hr, int64_t nranges, int swz,
-                                                          float* __restrict__ part) {
-    constexpr int E = NEB * 16;
-    constexpr int CH = E / 8;         // 16-byte chunks per W row
-    constexpr int NCH = range_width(E) / 32;   // K-chunks of a full range (the last range may be shorter)
-    __shared__ __attribute__((aligned(16))) uint16_t wsm[kLdsElems];
+struct Ring {
+    static constexpr int E = NEB * 16;
+    static constexpr int WCH = 64 * E;                       // bytes of one W chunk
+    static constexpr int WLOADS = WCH / 1024;                // wave loads per W chunk
+    static constexpr int DEPTH0 = (WAVE_LDS - 4096) / WCH;   // W slots that fit beside the X slots
+    static constexpr int DEPTH = DEPTH0 >= 8 ? 8 : DEPTH0 >= 4 ? 4 : 2;   // power of two
+    static constexpr int XPAIRS = DEPTH / 2;                 // X slots (one per chunk pair)
+    static_assert(DEPTH * WCH + XPAIRS * 1024 <= WAVE_LDS, "the wave's ring must fit its LDS share");
+};
 
-    const int64_t tb = blockIdx.x / nranges;
-    const int64_t rg = blockIdx.x - tb * nranges;
-    const int64_t h0 = rg * hr;
-    const int hlen = int(Hd - h0 < hr ? Hd - h0 : hr);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int NEB, int K>
+__global__ __launch_bounds__(NWAVE * 64) void moe_gate_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ wg, int64_t T,
+                                                              int64_t Hd, int k, int swz, int32_t* __restrict__ idx,
+                                                              float* __restrict__ wout, float* __restrict__ scores) {
+    using R = Ring<NEB>;
+    constexpr int E = R::E;
+    constexpr int DEPTH = R::DEPTH;
+    constexpr int LPS = 2 * R::WLOADS + 1;    // direct loads per chunk pair (two W chunks + one X pair)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NWAVE * WAVE_LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
+    const int64_t t0 = int64_t(blockIdx.x) * TB;
 
-    // Issue every load of the workgroup before waiting on any: the W slice goes to LDS,
-    // the X operands to registers.
-    //
-    // W[h0 .. h0 + hlen) is row-major [hd][E] in LDS with its 16-byte chunks swizzled
-    // per row. When a row has a power-of-two number of chunks, direct global-to-LDS
-    // loads fill it (one wave instruction = 1 KiB = 64 / CH rows; lane i lands in row
-    // i / CH, physical chunk i % CH, so it fetches the logical chunk that maps there).
-    if constexpr ((CH & (CH - 1)) == 0) {
-        constexpr int RPW = 64 / CH;
-        const int nwl = hlen / RPW;
-        for (int wl = wave; wl < nwl; wl += 4) {
-            const int r0 = wl * RPW;
-            const int row = r0 + lane / CH;
-            const int ch = (lane % CH) ^ (((row & 3) << 1) & swz);
-            lds_dma16(wg + (h0 + row) * E + ch * 8, &wsm[r0 * E]);
-        }
-    } else {
-        for (int i0 = 0; i0 < hlen * CH; i0 += 8 * 256) {
-            u32x4 val[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * 256 + tid;
-                if (i < hlen * CH) {
-                    const int row = i / CH, ch = i - row * CH;
-                    val[u] = *reinterpret_cast<const u32x4*>(wg + (h0 + row) * E + ch * 8);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * 256 + tid;
-                if (i < hlen * CH) {
-                    const int row = i / CH, ch = i - row * CH;
-                    *reinterpret_cast<u32x4*>(&wsm[row * E + ch * 8]) = val[u];   // no swizzle (swz = 0)
-                }
-            }
-        }
-    }
+    unsigned char* const ring = smem + wave * WAVE_LDS;
+    unsigned char* const wslots = ring;                       // DEPTH x WCH
+    unsigned char* const xslots = ring + DEPTH * R::WCH;      // XPAIRS x 1 KiB
 
-    // A operand: lane (token l16 of this wave's 16, group g) holds X[token][h0 + 32c + 8g .. +7].
-    int64_t tok = tb * TBM + 16 * wave + l16;
-    tok = tok < T ? tok : T - 1;
-    const uint16_t* xr = x + tok * Hd + h0 + 8 * g;
-    const int nc = hlen / 32;                 // <= NCH
-    u32x4 xa[NCH];
+    // This wave's contiguous share of the hidden axis, in 32-wide chunks, taken in pairs.
+    const int64_t nch = Hd / 32;
+    const int64_t per = (nch + NWAVE - 1) / NWAVE;
+    const int64_t c_begin = wave * per < nch ? wave * per : nch;
+    const int64_t c_end = c_begin + per < nch ? c_begin + per : nch;
+    const int my = int(c_end - c_begin);      // chunks of this wave (wave-uniform)
+    const int npairs = (my + 1) / 2;
+
+    // X pair loads: lane i fetches token i / 8 (clamped to T - 1), 16 bytes of its 128-byte row of
+    // the pair's 64 hidden values; it lands at physical piece (i % 8) of token row i / 8, so it
+    // fetches the logical piece (i % 8) ^ (token & 7). The wave-uniform base is token t0's row.
+    const int xt = lane >> 3;
+    int64_t xtok = t0 + xt;
+    xtok = xtok < T ? xtok : T - 1;
+    const int64_t tb0 = t0 < T ? t0 : T - 1;
+    const int x_lp = ((lane & 7) ^ xt) & 7;   // the logical piece this lane fetches
+    const uint32_t x_row = uint32_t((xtok - tb0) * Hd * 2);   // < 2^32: the host bounds Hd below 2^26
+    const uint16_t* xw = x + tb0 * Hd;        // wave-uniform
+    // W chunk loads: lane i of wave load l lands in chunk row (l * 1024 + 16 i) / (2E), physical
+    // 16-byte chunk ((l * 1024 + 16 i) % (2E)) / 16, and fetches the logical chunk mapped there.
+    uint32_t w_lane[R::WLOADS];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int cc = c < nc ? c : nc - 1;   // the tail range re-reads its last chunk (unused)
-        xa[c] = *reinterpret_cast<const u32x4*>(xr + 32 * cc);
+    for (int l = 0; l < R::WLOADS; ++l) {
+        const int byte = l * 1024 + 16 * lane;
+        const int row = byte / (2 * E);
+        const int pc = (byte % (2 * E)) / 16;
+        const int lc = pc ^ (((row & 3) << 1) & swz);
+        w_lane[l] = uint32_t(row * E * 2 + lc * 16);
     }
+    auto issue_pair = [&](int p) {            // chunks 2p and 2p + 1 of this wave (npairs >= 1)
+        const int pc = p < npairs ? p : npairs - 1;
+        const int64_t c0 = c_begin + 2 * pc;
+        const uint32_t xs = lds_addr(xslots) + uint32_t((p % R::XPAIRS) * 1024);
+        // A pair whose second chunk is past the hidden axis (an odd chunk count) fetches the
+        // first chunk's pieces in its place (unused), so no load runs past the end of X.
+        const int lp = (c0 + 1 >= nch && x_lp >= 4) ? x_lp - 4 : x_lp;
+        lds_dma16_sb(xw, x_row + uint32_t(c0 * 64 + lp * 16), xs);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int64_t c = c0 + h;
+            c = c < c_end ? c : c_end - 1;    // the odd tail re-reads the last chunk (unused)
+            const uint16_t* wsrc = wg + c * 32 * E;
+            const uint32_t ws = lds_addr(wslots) + uint32_t(((2 * p + h) % DEPTH) * R::WCH);
+#pragma unroll
+            for (int l = 0; l < R::WLOADS; ++l) lds_dma16_sb(wsrc, w_lane[l], ws + uint32_t(l * 1024));
+        }
+    };
 
     f32x4 acc[NEB];
 #pragma unroll
     for (int b = 0; b < NEB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Only the W slice must be complete before the barrier: the X loads were issued after
-    // it, so waiting until NCH loads remain leaves exactly the X chunks in flight. Chunk c
-    // of X is then waited for just before its MFMAs (the compiler counts those loads), so
-    // the matrix work on the first chunks overlaps the arrival of the later ones. (The W
-    // loads are issued through inline assembly, which keeps the compiler from waiting for
-    // every load before the first LDS read.)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
-    __syncthreads();
 
-    const int j = l16;
-    // Full ranges take a loop without a chunk test (so no load is sunk below the
-    // barrier); only the last, shorter range skips the chunks past its end.
-    auto mfma_chunks = [&](auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
+    // B operand offsets: lane (expert l16 of block b, group g) holds W[8g + e][16b + l16], read
+    // as rows 8g + j/4 and 8g + 4 + j/4, columns 16b + 4(j%4) .. +3 of a 16-lane group (j = l16).
+    int b_off[NEB][2];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            if (!FULL && c >= nc) continue;
-            // B operand: lane (expert l16 of block b, group g) holds W[32c + 8g + e][16b + l16];
-            // group lane j reads rows 32c + 8g + j/4 (+4), columns 16b + 4(j%4) .. +3.
-            const int r0 = 32 * c + 8 * g + (j >> 2);
-            const int r1 = r0 + 4;
+    for (int b = 0; b < NEB; ++b) {
+        const int r0 = 8 * g + (l16 >> 2), r1 = r0 + 4;
+        const int col = 16 * b + 4 * (l16 & 3);
+        b_off[b][0] = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
+        b_off[b][1] = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
+    }
+    // A operand: lane (token l16 & 7, group g) reads the 8 hidden values 32h + 8g .. +7 of its token
+    // (h = the chunk within the pair): logical piece 4h + g of the token's row. Rows 8..15 of the
+    // 16-row MFMA repeat tokens 0..7; their results are not used.
+    const int at = l16 & 7;
+    const int a_off[2] = {at * 128 + ((((0 + g) ^ at) & 7) * 16), at * 128 + ((((4 + g) ^ at) & 7) * 16)};
+
+    // Prologue: DEPTH / 2 - 1 pairs in flight. (A wave with no chunks, when the hidden axis is
+    // shorter than 4 chunks, loads nothing and contributes zeros.)
+    if (npairs > 0) {
 #pragma unroll
-            for (int b = 0; b < NEB; ++b) {
-                const int col = 16 * b + 4 * (j & 3);
-                const int p0 = r0 * E + ((((col >> 3) ^ (((r0 & 3) << 1) & swz))) << 3) + (col & 7);
-                const int p1 = r1 * E + ((((col >> 3) ^ (((r1 & 3) << 1) & swz))) << 3) + (col & 7);
-                const bf16x4_t lo = lds_read_tr16(wsm + p0);
-                const bf16x4_t hi = lds_read_tr16(wsm + p1);
-                const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[c]),
-                                                                  __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0, 0);
+        for (int p = 0; p < DEPTH / 2 - 1; ++p) issue_pair(p);
+    }
+    for (int p = 0; p < npairs; ++p) {
+        issue_pair(p + DEPTH / 2 - 1);        // into the slots pair p - 1 used (read last iteration)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH / 2 - 1) * LPS) : "memory");   // pair p is in
+        const unsigned char* xs = xslots + (p % R::XPAIRS) * 1024;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (2 * p + h < my) {
+                const uint16_t* ws = reinterpret_cast<const uint16_t*>(wslots + ((2 * p + h) % DEPTH) * R::WCH);
+                const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xs + a_off[h]);
+#pragma unroll
+                for (int b = 0; b < NEB; ++b) {
+                    const bf16x4_t lo = lds_read_tr16(ws + b_off[b][0]);
+                    const bf16x4_t hi = lds_read_tr16(ws + b_off[b][1]);
+                    const bf16x8_t wb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, wb), acc[b], 0, 0,
+                                                                      0);
+                }
             }
         }
-    };
-    if (nc == NCH) mfma_chunks(std::true_type{});
-    else mfma_chunks(std::false_type{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // retire the trailing (unused) loads
 
-    // acc[b][r] = partial score of token (16*wave + 4g + r) for expert 16b + l16.
-    float* pblk = part + ((tb * nranges + rg) * TBM) * E;
+    // acc[b][r] = partial score of token 4g + r (g < 2: tokens 0..7) for expert 16b + l16. The
+    // waves' partials meet in LDS ([wave][token][expert] fp32; the rings are free after the
+    // barrier) and are added in wave order.
+    __syncthreads();
+    float* part = reinterpret_cast<float*>(smem);
+    if (g < 2) {
 #pragma unroll
-    for (int b = 0; b < NEB; ++b)
+        for (int b = 0; b < NEB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pblk[(16 * wave + 4 * g + r) * E + 16 * b + l16] = acc[b][r];
+            for (int r = 0; r < 4; ++r) part[(wave * TB + 4 * g + r) * E + 16 * b + l16] = acc[b][r];
+    }
+    __syncthreads();
 
-}
-
-// Phase 2: sixteen lanes per token (4 tokens per wave, one wave per workgroup, so 2048
-// tokens spread over 512 workgroups); lane q of a token owns experts [q * NEB, q * NEB + NEB).
-constexpr int RED_T = 64;             // threads per reduce workgroup
-
-template <int NEB, int K>
-__global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restrict__ part, int64_t T, int64_t nranges,
-                                                         int k, int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                         float* __restrict__ scores) {
-    constexpr int E = NEB * 16;
-    const int tid = threadIdx.x;
-    const int q = tid & 15;
-    const int64_t t_out = int64_t(blockIdx.x) * (RED_T / 16) + (tid >> 4);
-    const bool valid = t_out < T;
+    // Sixteen lanes per token (waves 0 and 1: 128 threads for 8 tokens); lane q of a token owns
+    // experts q * NEB .. q * NEB + NEB - 1.
+    if (tid >= TB * 16) return;               // whole waves only: no barrier follows
+    const int tok = tid >> 4, q = tid & 15;
+    const int64_t t_out = t0 + tok;
     float ts[K];
     int ti[K];
 #pragma unroll
@@ -219,34 +211,14 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
         ts[r] = kNegInf;
         ti[r] = 0x7FFFFFFF;
     }
-    if (valid) {
-        // Sum the range partials in range order (deterministic), loading RB ranges' worth
-        // of this lane's experts before adding, so the loads overlap.
-        const int64_t tb = t_out / TBM;
-        const int64_t tl = t_out - tb * TBM;
-        const float* base = part + (tb * nranges * TBM + tl) * E + q * NEB;
-        constexpr int RB = NEB >= 8 ? 4 : 8;
-        float sum[NEB];
 #pragma unroll
-        for (int e = 0; e < NEB; ++e) sum[e] = 0.f;
-        for (int64_t r0 = 0; r0 < nranges; r0 += RB) {
-            float buf[RB][NEB];
+    for (int e = 0; e < NEB; ++e) {
+        const int ex = q * NEB + e;
+        float s = part[tok * E + ex];
 #pragma unroll
-            for (int rr = 0; rr < RB; ++rr)
-                if (r0 + rr < nranges)
-#pragma unroll
-                    for (int e = 0; e < NEB; ++e) buf[rr][e] = base[(r0 + rr) * TBM * E + e];
-#pragma unroll
-            for (int rr = 0; rr < RB; ++rr)
-                if (r0 + rr < nranges)
-#pragma unroll
-                    for (int e = 0; e < NEB; ++e) sum[e] += buf[rr][e];
-        }
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) {
-            if (scores) scores[t_out * E + q * NEB + e] = sum[e];
-            topk_insert<K>(ts, ti, sum[e], q * NEB + e);
-        }
+        for (int w = 1; w < NWAVE; ++w) s += part[(w * TB + tok) * E + ex];
+        if (scores && t_out < T) scores[t_out * E + ex] = s;
+        topk_insert<K>(ts, ti, s, ex);
     }
     // Merge the sixteen lanes' lists of a token (lanes differing in bits 0-3).
 #pragma unroll
@@ -261,9 +233,9 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
 #pragma unroll
         for (int r = 0; r < K; ++r) topk_insert<K>(ts, ti, os[r], oi[r]);
     }
-    // The list holds the K best; the first k (k <= K) are the output, and the
-    // softmax runs over exactly those k scores.
-    if (valid && q == 0) {
+    // The list holds the K best; the first k (k <= K) are the output, and the softmax runs over
+    // exactly those k scores.
+    if (t_out < T && q == 0) {
         float den = 0.f;
         float ex[K];
 #pragma unroll
@@ -283,39 +255,29 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
 }
 
 template <int NEB>
-hipError_t launch_e(int k, const MoeGeom& g, int swz, hipStream_t stream, const uint16_t* x, const uint16_t* w,
-                    int64_t T, int64_t Hd, int32_t* idx, float* wout, float* scores, float* part) {
-    const dim3 grid1{unsigned(g.ntb * g.nranges), 1u, 1u};
-    hipLaunchKernelGGL((moe_partial_kernel<NEB>), grid1, dim3(256), 0, stream, x, w, T, Hd, g.hr, g.nranges, swz,
-                       part);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 grid2{unsigned(ceil_div(T, int64_t(RED_T / 16))), 1u, 1u};
+hipError_t launch_e(int k, int swz, hipStream_t stream, const uint16_t* x, const uint16_t* w, int64_t T, int64_t Hd,
+                    int32_t* idx, float* wout, float* scores) {
+    const dim3 grid{unsigned(ceil_div(T, TB)), 1u, 1u};
     // A top-2 fast path; any other k up to 8 keeps an 8-entry list.
     if (k == 2)
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 2>), grid2, dim3(RED_T), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_gate_kernel<NEB, 2>), grid, dim3(NWAVE * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
                            scores);
     else
-        hipLaunchKernelGGL((moe_reduce_kernel<NEB, 8>), grid2, dim3(RED_T), 0, stream, part, T, g.nranges, k, idx, wout,
+        hipLaunchKernelGGL((moe_gate_kernel<NEB, 8>), grid, dim3(NWAVE * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
                            scores);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t moe_workspace_bytes(int64_t T, int64_t Hd, int64_t E) {
-    return moe_geom(T, Hd, E).part_bytes;
-}
-
 hipError_t launch_moe_route(const uint16_t* x, const uint16_t* w_gate, int64_t T, int64_t Hd, int E, int k,
-                            int32_t* idx, float* w, float* scores, void* workspace, hipStream_t stream) {
-    const MoeGeom g = moe_geom(T, Hd, E);
-    if (g.ntb * g.nranges > INT32_MAX || ceil_div(T, int64_t(RED_T / 16)) > INT32_MAX) return hipErrorInvalidValue;
+                            int32_t* idx, float* w, float* scores, hipStream_t stream) {
+    if (ceil_div(T, TB) > INT32_MAX) return hipErrorInvalidValue;
     const int CH = E / 8;
+    // Swizzle the W chunks only when a row has a power-of-two count (>= 8) of 16-byte chunks.
     const int swz = (CH >= 8 && (CH & (CH - 1)) == 0) ? 6 : 0;
-    float* part = static_cast<float*>(workspace);
 #define RF_MOE_E(NB) \
-    case NB: return launch_e<NB>(k, g, swz, stream, x, w_gate, T, Hd, idx, w, scores, part);
+    case NB: return launch_e<NB>(k, swz, stream, x, w_gate, T, Hd, idx, w, scores);
     switch (E / 16) {
         RF_MOE_E(1) RF_MOE_E(2) RF_MOE_E(3) RF_MOE_E(4) RF_MOE_E(5) RF_MOE_E(6) RF_MOE_E(7) RF_MOE_E(8)
         RF_MOE_E(9) RF_MOE_E(10) RF_MOE_E(11) RF_MOE_E(12) RF_MOE_E(13) RF_MOE_E(14) RF_MOE_E(15) RF_MOE_E(16)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 3
+#define RF_ABI_VERSION 4
 
 /* Exported symbols (the library is built with hidden visibility by default). */
 #if defined(__GNUC__) || defined(__clang__)
@@ -339,37 +339,52 @@ RF_API rf_status rf_cascade_gemm(rf_cascade_gemm_kind kind, const float* x, cons
                                  int64_t N, float* y, float* stat, rf_stream stream);
 
 /*
- * rf_moe_route_workspace_size -- bytes of device workspace rf_moe_route needs.
- */
-RF_API size_t rf_moe_route_workspace_size(int64_t T, int64_t Hd, int64_t E);
-
-/*
  * rf_moe_route -- fused MoE gate: scores = X W_gate -> top-k -> softmax over the k.
  *
- * The cascade of the explainer's section 4.2; the full score matrix never
- * reaches memory (unless the optional debug output is requested). Experts are
+ * The cascade of the explainer's section 4.2 in a single kernel: the score matrix
+ * never reaches memory (unless the optional debug output is requested). Experts are
  * ordered by descending score, equal scores by the lower expert index. The
  * weights are the softmax of the k selected scores:
  * w_r = exp(s_r - s_1) / sum_r' exp(s_r' - s_1). Scores accumulate in fp32.
  *
- * The hidden axis is split into ranges (the Multi-Segment strategy of the
- * technical summary, Methodologie 3, applied to the gate GEMM's sum): a first
- * launch writes one partial score block per (64-token block, hidden range) to
- * `workspace`; a second adds each token's partials in a fixed order
- * (deterministic) and performs the top-k and the softmax.
+ * Each workgroup owns 8 tokens and every expert: its waves split the hidden axis
+ * (the Multi-Segment strategy of the technical summary, Methodologie 3, inside one
+ * workgroup), add their partial scores on chip in a fixed order (deterministic) and
+ * select and normalise the k best. No workspace is needed. Every workgroup reads all of
+ * W_gate from L2; rf_moe_route_split gives each workgroup one range of it instead and
+ * exchanges partial scores through a workspace in two launches (measured beside it).
  *
  *   x       [T, Hd] bf16 tokens.   w_gate  [Hd, E] bf16 (expert index contiguous).
  *   idx     [T, k] int32 expert indices.   w  [T, k] fp32 weights.
  *   scores  [T, E] fp32 debug copy of the gate scores, or NULL.
- *   workspace, ws_bytes  device scratch of at least rf_moe_route_workspace_size(T, Hd, E)
- *           bytes (RF_ERR_BUFFER_TOO_SMALL otherwise); no initial contents are
- *           required. Calls that share a workspace must not run concurrently.
- *   Supported: T >= 1; Hd >= 32 and Hd % 32 == 0; 16 <= E <= 256 and E % 16 == 0;
+ *   Supported: T >= 1; 32 <= Hd < 2^26 and Hd % 32 == 0; 16 <= E <= 256 and E % 16 == 0;
  *   1 <= k <= min(8, E).
  */
 RF_API rf_status rf_moe_route(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E,
-                       int64_t k, int32_t* idx, float* w, float* scores, void* workspace,
-                       size_t ws_bytes, rf_stream stream);
+                              int64_t k, int32_t* idx, float* w, float* scores, rf_stream stream);
+
+/*
+ * rf_moe_route_split_workspace_size -- bytes of device workspace rf_moe_route_split needs.
+ */
+RF_API size_t rf_moe_route_split_workspace_size(int64_t T, int64_t Hd, int64_t E);
+
+/*
+ * rf_moe_route_split -- rf_moe_route in two launches over a split hidden axis (the
+ * Multi-Segment strategy of the technical summary, Methodologie 3, across workgroups and
+ * the multi-kernel level of the explainer's section 3.3), for comparison with the
+ * one-launch form: a first launch writes one partial score block per (64-token block,
+ * hidden range) to `workspace`, a second adds each token's partials in a fixed order
+ * (deterministic) and performs the top-k and the softmax. Each workgroup reads only its
+ * range of W_gate, which on MI355X outweighs the partials' round trip: see rf_moe_route.
+ *
+ *   Arguments and results as for rf_moe_route, plus:
+ *   workspace, ws_bytes  device scratch of at least rf_moe_route_split_workspace_size(T, Hd, E)
+ *           bytes (RF_ERR_BUFFER_TOO_SMALL otherwise); no initial contents are required.
+ *           Calls that share a workspace must not run concurrently.
+ */
+RF_API rf_status rf_moe_route_split(const void* x, const void* w_gate, int64_t T, int64_t Hd, int64_t E,
+                                    int64_t k, int32_t* idx, float* w, float* scores, void* workspace,
+                                    size_t ws_bytes, rf_stream stream);
 
 /*
  * rf_quant_gemm_workspace_size -- bytes of device workspace rf_quant_gemm needs

@@ -33,8 +33,7 @@ def test_header_declares_the_boundary():
         "rf_attn_decode_split", "rf_segment_merge", "rf_attn_decode_segments", "rf_mla_decode_split", "rf_row_cascade",
         "rf_cascade_gemm",
         "rf_attn_decode_workspace_size", "rf_attn_decode", "rf_attn_decode_noalloc",
-        "rf_moe_route_workspace_size",
-        "rf_moe_route",
+        "rf_moe_route", "rf_moe_route_split_workspace_size", "rf_moe_route_split",
         "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
 
 
@@ -45,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rf_abi_version() == 3
+    assert lib.rf_abi_version() == 4
     for code, name in [(0, b"RF_OK"), (1, b"RF_ERR_INVALID_ARGUMENT"), (2, b"RF_ERR_UNSUPPORTED"),
                        (3, b"RF_ERR_BUFFER_TOO_SMALL"), (4, b"RF_ERR_DEVICE")]:
         assert lib.rf_status_string(code) == name
@@ -109,8 +108,8 @@ def test_merge_validation(lib):
     assert _merge(lib, lse=P4 + 16) == INVALID
 
 
-def _moe(lib, x=P, w=P2, T=8, Hd=64, E=64, k=2, idx=P3, wt=P4, sc=None, ws=P6, nbytes=1 << 20):
-    return lib.rf_moe_route(x, w, T, Hd, E, k, idx, wt, sc, ws, nbytes, None)
+def _moe(lib, x=P, w=P2, T=8, Hd=64, E=64, k=2, idx=P3, wt=P4, sc=None):
+    return lib.rf_moe_route(x, w, T, Hd, E, k, idx, wt, sc, None)
 
 
 def test_moe_validation(lib):
@@ -119,16 +118,20 @@ def test_moe_validation(lib):
     assert _moe(lib, k=65) == INVALID
     assert _moe(lib, k=9) == UNSUPPORTED
     assert _moe(lib, Hd=48) == UNSUPPORTED
+    assert _moe(lib, Hd=1 << 26) == UNSUPPORTED
     assert _moe(lib, E=40) == UNSUPPORTED
     assert _moe(lib, E=512) == UNSUPPORTED
     assert _moe(lib, T=0) == INVALID
     assert _moe(lib, idx=P4) == INVALID                     # idx aliases w
     assert _moe(lib, sc=P + 16) == INVALID                  # scores inside x
-    need = lib.rf_moe_route_workspace_size(2048, 4096, 64)
+    s = lib.rf_moe_route_split
+    need = lib.rf_moe_route_split_workspace_size(2048, 4096, 64)
     assert need == 32 * 8 * 64 * 64 * 4                    # 32 token blocks x 8 hidden ranges of partial scores
-    assert _moe(lib, ws=None) == TOO_SMALL
-    assert _moe(lib, nbytes=lib.rf_moe_route_workspace_size(8, 64, 64) - 1) == TOO_SMALL
-    assert _moe(lib, ws=P + 64) == INVALID                  # workspace inside x
+    assert s(P, P2, 8, 64, 64, 2, P3, P4, None, None, 1 << 20, None) == TOO_SMALL
+    assert s(P, P2, 8, 64, 64, 2, P3, P4, None, P6, lib.rf_moe_route_split_workspace_size(8, 64, 64) - 1,
+             None) == TOO_SMALL
+    assert s(P, P2, 8, 64, 64, 2, P3, P4, None, P + 64, 1 << 20, None) == INVALID   # workspace inside x
+    assert s(P, P2, 8, 48, 64, 2, P3, P4, None, P6, 1 << 20, None) == UNSUPPORTED   # Hd 48
 
 
 def _qg(lib, x=P, wq=P2, ws=P3, M=16, N=16, K=256, y=P4, xs=P5, xq=P6, work=None, nbytes=0):

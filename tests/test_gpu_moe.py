@@ -17,8 +17,9 @@ pytestmark = pytest.mark.gpu
 ATOL, RTOL = 2e-2, 1e-2
 
 
-def _check(rf, x, w, k, check_scores=True):
-    idx, wt, sc = rf.moe_route(dev_bf16(x), dev_bf16(w), k, return_scores=check_scores)
+def _check(rf, x, w, k, check_scores=True, split=False):
+    route = rf.moe_route_split if split else rf.moe_route
+    idx, wt, sc = route(dev_bf16(x), dev_bf16(w), k, return_scores=check_scores)
     torch.cuda.synchronize()
     xf = bf16_bits_to_f32(x).astype(np.float64)
     wf = bf16_bits_to_f32(w).astype(np.float64)
@@ -39,10 +40,15 @@ def _check(rf, x, w, k, check_scores=True):
     (77, 1024, 48, 3),     # E not a power of two
     (300, 160, 32, 5),     # hidden size not a multiple of the range
     (50, 128, 128, 1),
+    (20, 32, 16, 2),       # one hidden chunk: three of the four waves have none
+    (40, 96, 64, 2),       # three chunks: one per wave, the last wave idle
+    (9, 224, 80, 3),       # seven chunks: the last wave's chunk count is odd
+    (1000, 2048, 64, 2),   # many workgroups
 ])
-def test_route_shapes(rf, T, Hd, E, k):
+@pytest.mark.parametrize("split", [False, True], ids=["one_launch", "split"])
+def test_route_shapes(rf, T, Hd, E, k, split):
     x, w = moe_inputs(T, Hd, E, k, seed=900 + T + E + k, w_std=0.5 if Hd < 1024 else 0.02)
-    _check(rf, x, w, k)
+    _check(rf, x, w, k, split=split)
 
 
 def test_exact_ties_prefer_lower_index(rf):
@@ -63,8 +69,8 @@ def test_exact_ties_prefer_lower_index(rf):
     assert ties > 0
 
 
-def test_repeated_calls_reuse_workspace(rf):
-    """Back-to-back calls on one (dirty) workspace agree."""
+def test_repeated_calls_agree(rf):
+    """Back-to-back calls agree bit for bit, and a smaller call after them is still right."""
     x, w = moe_inputs(256, 512, 64, 2, seed=31, w_std=0.5)
     a = _check(rf, x, w, 2, check_scores=False)
     b = _check(rf, x, w, 2, check_scores=False)
@@ -73,8 +79,18 @@ def test_repeated_calls_reuse_workspace(rf):
     _check(rf, x2, w2, 2, check_scores=False)
 
 
-def test_moe_workload(rf):
+@pytest.mark.parametrize("split", [False, True], ids=["one_launch", "split"])
+def test_moe_workload(rf, split):
     """The routing workload: 2048 tokens x 4096 hidden, 64 experts, top-2."""
     c = CONFIGS["C4"]
     x, w = moe_inputs(c["T"], c["Hd"], c["E"], c["k"], c["seed"])
-    _check(rf, x, w, c["k"])
+    _check(rf, x, w, c["k"], split=split)
+
+
+def test_forms_agree(rf):
+    """The one-launch and the two-launch forms select the same experts and agree on the weights."""
+    x, w = moe_inputs(500, 1024, 64, 2, seed=33, w_std=0.02)
+    a = _check(rf, x, w, 2, check_scores=False)
+    b = _check(rf, x, w, 2, check_scores=False, split=True)
+    assert np.array_equal(a[0], b[0])
+    assert_close(b[1], a[1], 1e-5, 1e-5, "weights of the two forms")
