@@ -21,7 +21,7 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 4
+ABI_VERSION = 5
 RF_F32, RF_BF16 = 0, 1
 _STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARGUMENT", 2: "RF_ERR_UNSUPPORTED",
            3: "RF_ERR_BUFFER_TOO_SMALL", 4: "RF_ERR_DEVICE"}
@@ -61,6 +61,7 @@ _SIGS = {
     "rf_moe_route_split": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
     "rf_quant_gemm_workspace_size": ([_I64, _I64, _I64], _SZ),
     "rf_quant_gemm": ([_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _c.c_int),
+    "rf_quant_gemm_fused": ([_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
 }
 
 
@@ -435,4 +436,26 @@ def quant_gemm(x, wq, w_scale, *, y=None, x_scale=None, xq=None, workspace=None,
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().rf_quant_gemm(_ptr(x), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y), _ptr(x_scale), _ptr(xq),
                                 _ptr(workspace), ws_bytes, _stream(x)))
+    return y, x_scale, xq
+
+
+def quant_gemm_fused(x, wq, w_scale, *, y=None, x_scale=None, xq=None, return_codes: bool = False):
+    """The same cascade as quant_gemm in one launch, with no workspace (rf_quant_gemm_fused)."""
+    torch = _torch()
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(wq, "wq", torch.uint8, (N, K))
+    _need(w_scale, "w_scale", torch.float32, (N,))
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    x_scale = torch.empty((M,), dtype=torch.float32, device=dev) if x_scale is None else x_scale
+    _need(y, "y", torch.bfloat16, (M, N))
+    _need(x_scale, "x_scale", torch.float32, (M,))
+    if xq is None and return_codes:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if xq is not None:
+        _need(xq, "xq", torch.uint8, (M, K))
+    _check(load().rf_quant_gemm_fused(_ptr(x), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y), _ptr(x_scale), _ptr(xq),
+                                      _stream(x)))
     return y, x_scale, xq

@@ -584,4 +584,30 @@ rf_status rf_quant_gemm(const void* x, const uint8_t* wq, const float* w_scale, 
     return device_status(e, "rf_quant_gemm GEMM launch");
 }
 
+rf_status rf_quant_gemm_fused(const void* x, const uint8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                              int64_t K, void* y, float* x_scale, uint8_t* xq, rf_stream stream) {
+    RF_PTR(x, "x");
+    RF_PTR(wq, "wq");
+    RF_PTR(w_scale, "w_scale");
+    RF_PTR(y, "y");
+    RF_PTR(x_scale, "x_scale");
+    RF_OPT_PTR(xq, "xq");
+    RF_REQUIRE(M >= 1 && N >= 1 && K >= 1, RF_ERR_INVALID_ARGUMENT, "M, N and K must be >= 1");
+    RF_REQUIRE(K % 128 == 0, RF_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)K);
+    int64_t nx, nw, ny;
+    RF_REQUIRE(prod({M, K}, &nx) && nx < kMaxElems && prod({N, K}, &nw) && nw < kMaxElems &&
+                   prod({M, N}, &ny) && ny < kMaxElems && M <= INT32_MAX && N <= INT32_MAX,
+               RF_ERR_UNSUPPORTED, "tensor too large");
+    const size_t nq = xq ? size_t(nx) : 0;
+    RF_REQUIRE(!overlap(y, ny * 2, x, nx * 2) && !overlap(y, ny * 2, wq, nw) && !overlap(y, ny * 2, w_scale, N * 4) &&
+                   !overlap(x_scale, M * 4, x, nx * 2) && !overlap(x_scale, M * 4, wq, nw) &&
+                   !overlap(x_scale, M * 4, y, ny * 2) && !overlap(x_scale, M * 4, w_scale, N * 4) &&
+                   !overlap(xq, nq, x, nx * 2) && !overlap(xq, nq, wq, nw) && !overlap(xq, nq, y, ny * 2) &&
+                   !overlap(xq, nq, x_scale, M * 4) && !overlap(xq, nq, w_scale, N * 4),
+               RF_ERR_INVALID_ARGUMENT, "outputs must not alias inputs or each other");
+    hipError_t e = rf::launch_quant_gemm_fused(static_cast<const uint16_t*>(x), wq, w_scale, M, N, K,
+                                               static_cast<uint16_t*>(y), x_scale, xq, static_cast<hipStream_t>(stream));
+    return device_status(e, "rf_quant_gemm_fused launch");
+}
+
 }  // extern "C"

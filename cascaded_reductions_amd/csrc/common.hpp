@@ -87,18 +87,21 @@ __device__ __forceinline__ float row8_sum(float v) {
 // an explicit "s_waitcnt vmcnt(N)" and a barrier (vmcnt retires loads in issue order,
 // so loads the compiler does not know of can only make its own waits stricter).
 // The LDS base goes to M0 through the "{m0}" operand constraint, so the compiler sets M0
-// itself and knows the value it holds.
+// itself and knows the value it holds. A global load to LDS needs one wait state after a
+// scalar write of M0, which the compiler emits right before the assembly and does not
+// check against it, so the wait state is part of it.
 __device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds_base)));
-    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(base) : "memory");
 }
 
 // The same with a wave-uniform 64-bit global base (SGPR pair) and a per-lane 32-bit
 // byte offset: the address costs no vector instruction. A vector-memory instruction that
 // reads an SGPR written by a vector instruction (v_readfirstlane_b32, which the compiler
 // uses when it forms the base in VGPRs) needs 5 wait states, and the compiler's hazard
-// check does not see the operands of inline assembly, so the wait states are part of it.
+// check does not see the operands of inline assembly, so the wait states (which also
+// cover the one after the M0 write) are part of it.
 __device__ __forceinline__ void lds_dma16_sb(const void* gbase, uint32_t voff_bytes, uint32_t lds_base) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff_bytes), "s"(gbase), "{m0}"(lds_base)
                  : "memory");

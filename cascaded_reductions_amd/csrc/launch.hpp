@@ -66,5 +66,8 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* c
 // FP8 GEMM with per-row / per-column dequantisation: y[M,N] bf16 = (a[M,K] . b[N,K]^T) * sa[m] * sb[n].
 hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
                            int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// Both steps in one launch: x [M, K] bf16 -> y, x_scale [M] and (when xq is not null) the codes.
+hipError_t launch_quant_gemm_fused(const uint16_t* x, const uint8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                                   int64_t K, uint16_t* y, float* x_scale, uint8_t* xq, hipStream_t stream);
 
 }  // namespace rf

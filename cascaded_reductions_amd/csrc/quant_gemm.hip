@@ -61,6 +61,32 @@ __device__ __forceinline__ float div_rn(float x, float sigma, float r) {
     return __builtin_copysignf(fmaf(e, r, q0), x);
 }
 
+// Eight bf16 values of a row -> eight E4M3FN codes (two dwords, in order), all +0 for a
+// zero row. Shared by both forms of the cascade, so their codes agree bit for bit.
+__device__ __forceinline__ uint2 codes8(const u32x4& t, float sigma, float r) {
+    uint32_t out0 = 0u, out1 = 0u;
+    if (sigma >= kMinRecipSigma) {
+        float q[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            q[2 * w] = div_rn(bf16_lo(t[w]), sigma, r);
+            q[2 * w + 1] = div_rn(bf16_hi(t[w]), sigma, r);
+        }
+        out0 = codes4(q[0], q[1], q[2], q[3]);
+        out1 = codes4(q[4], q[5], q[6], q[7]);
+    } else if (sigma > 0.f) {                  // rows of tiny magnitude: IEEE division
+        float q[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            q[2 * w] = bf16_lo(t[w]) / sigma;
+            q[2 * w + 1] = bf16_hi(t[w]) / sigma;
+        }
+        out0 = codes4(q[0], q[1], q[2], q[3]);
+        out1 = codes4(q[4], q[5], q[6], q[7]);
+    }
+    return make_uint2(out0, out1);
+}
+
 // One wave per row, four rows per workgroup. NCT > 0: lane l holds chunks l, l + 64, ...
 // (at most NCT chunks of 8 values), all loaded before the first use so every 16-byte
 // load of the row is in flight at once, and the row stays in registers between the
@@ -108,29 +134,7 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
     const float r = 1.0f / sigma;              // IEEE fp32 division (inf for a zero row; unused then)
     if (lane == 0) xs[row] = sigma;
 
-    auto quant8 = [&](const u32x4& t, int ch) {
-        uint32_t out0 = 0u, out1 = 0u;
-        if (sigma >= kMinRecipSigma) {
-            float q[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                q[2 * w] = div_rn(bf16_lo(t[w]), sigma, r);
-                q[2 * w + 1] = div_rn(bf16_hi(t[w]), sigma, r);
-            }
-            out0 = codes4(q[0], q[1], q[2], q[3]);
-            out1 = codes4(q[4], q[5], q[6], q[7]);
-        } else if (sigma > 0.f) {              // rows of tiny magnitude: IEEE division
-            float q[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                q[2 * w] = bf16_lo(t[w]) / sigma;
-                q[2 * w + 1] = bf16_hi(t[w]) / sigma;
-            }
-            out0 = codes4(q[0], q[1], q[2], q[3]);
-            out1 = codes4(q[4], q[5], q[6], q[7]);
-        }
-        cr[ch] = make_uint2(out0, out1);
-    };
+    auto quant8 = [&](const u32x4& t, int ch) { cr[ch] = codes8(t, sigma, r); };
     if constexpr (NCT > 0) {
 #pragma unroll
         for (int i = 0; i < NCT; ++i) {
@@ -188,6 +192,104 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t total, int64_t tile
     tm = first + (in - tn * width);
 }
 
+// Operands of one K slice (32 code bytes of every row) in a wave's registers. Lane (row l32,
+// half g) holds the 16 bytes [32p + 16g, +16) of its rows; after the exact bf16 conversion,
+// bytes 0-7 feed the first K=16 MFMA of a pair and bytes 8-15 the second (the same
+// slot-to-k map for both operands). A wave owns a 128 (N) x 64 (M) block of the tile:
+// four 32-row W blocks (a) by two 32-row X blocks (b).
+struct SliceRegs {
+    u32x4 a[4], b[2];
+};
+struct Operands {
+    bf16x8 alo[4], ahi[4], blo[2], bhi[2];
+};
+__device__ __forceinline__ void convert(const SliceRegs& r, Operands& o) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        o.alo[a] = fp8x8_to_bf16(r.a[a][0], r.a[a][1]);
+        o.ahi[a] = fp8x8_to_bf16(r.a[a][2], r.a[a][3]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        o.blo[b] = fp8x8_to_bf16(r.b[b][0], r.b[b][1]);
+        o.bhi[b] = fp8x8_to_bf16(r.b[b][2], r.b[b][3]);
+    }
+}
+__device__ __forceinline__ void mfmas(const Operands& o, f32x16 (&acc)[4][2]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.alo[a], o.blo[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.ahi[a], o.bhi[b], acc[a][b], 0, 0, 0);
+        }
+}
+
+// acc[a][b][r] = C^T[n][m]: n = n0 + wn*128 + a*32 + (r/4)*8 + 4g + r%4, m = m0 + wm*64 + b*32 + l32.
+// Epilogue: scale by sigma_m (row_scale(local row)) and w_scale_n, round to bf16 and stage the
+// wave's 64 (m) x 128 (n) block in LDS (stg: 16 KiB per wave, free after the last barrier),
+// then write whole rows with 16-byte stores so every output line is written once and completely.
+template <class RowScale>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint8_t* stage_lds, RowScale row_scale,
+                                           const float* __restrict__ ws, int64_t M, int64_t N, int64_t m0,
+                                           int64_t n0, uint16_t* __restrict__ y) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int wn = wave >> 2, wm = wave & 3;
+    uint16_t* stg = reinterpret_cast<uint16_t*>(stage_lds) + wave * (64 * 128);
+    float wsc[4][4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int64_t n = n0 + wn * 128 + a * 32 + q4 * 8 + 4 * g + e;
+                n = n < N ? n : N - 1;
+                wsc[a][q4][e] = ws[n];
+            }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const float sx = row_scale(wm * 64 + b * 32 + l32);
+        const int ml = b * 32 + l32;           // row of the staging block
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int nl = a * 32 + q4 * 8 + 4 * g;   // column of the staging block (multiple of 4)
+                const f32x16& c = acc[a][b];
+                const uint2 w2 = make_uint2(
+                    pack_bf16x2((c[4 * q4 + 0] * sx) * wsc[a][q4][0], (c[4 * q4 + 1] * sx) * wsc[a][q4][1]),
+                    pack_bf16x2((c[4 * q4 + 2] * sx) * wsc[a][q4][2], (c[4 * q4 + 3] * sx) * wsc[a][q4][3]));
+                // 16-byte chunks of a staging row are rotated by the row index to spread banks.
+                const int chunk = ((nl >> 3) + ml) & 15;
+                *reinterpret_cast<uint2*>(stg + ml * 128 + chunk * 8 + (nl & 7)) = w2;
+            }
+    }
+    __syncthreads();
+    // 64 rows x 16 chunks of 16 bytes: each instruction writes 4 whole rows.
+    const int64_t nbase = n0 + wn * 128;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int ml = it * 4 + (lane >> 4);
+        const int ch = lane & 15;
+        const int64_t m = m0 + wm * 64 + ml;
+        const int64_t n = nbase + ch * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + ml * 128 + (((ch + ml) & 15) * 8));
+        if (m < M) {
+            uint16_t* dst = y + m * N + n;
+            if (n + 7 < N && ((N & 7) == 0)) {
+                *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+                const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = hv[e];
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq,
                                                       const float* __restrict__ xs, const float* __restrict__ ws,
                                                       int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -231,42 +333,15 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-    // One K slice = 32 code bytes of every row. Lane (row l32, half g) reads the 16 bytes
-    // [32p + 16g, +16) of its rows; after the exact bf16 conversion, bytes 0-7 feed the first
-    // K=16 MFMA of a pair and bytes 8-15 the second (the same slot-to-k map for both operands).
-    auto read_slice = [&](int st, int p, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
+    auto read_slice = [&](int st, int p, SliceRegs& r) {
         const uint8_t* sw = smem[st][0];
         const uint8_t* sx = smem[st][1];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-            ra[a] = *reinterpret_cast<const u32x4*>(sw + swz(wn * 128 + a * 32 + l32, 2 * p + g));
+            r.a[a] = *reinterpret_cast<const u32x4*>(sw + swz(wn * 128 + a * 32 + l32, 2 * p + g));
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-            rb[b] = *reinterpret_cast<const u32x4*>(sx + swz(wm * 64 + b * 32 + l32, 2 * p + g));
-    };
-    struct Operands {
-        bf16x8 alo[4], ahi[4], blo[2], bhi[2];
-    };
-    auto convert = [&](const u32x4 (&ra)[4], const u32x4 (&rb)[2], Operands& o) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            o.alo[a] = fp8x8_to_bf16(ra[a][0], ra[a][1]);
-            o.ahi[a] = fp8x8_to_bf16(ra[a][2], ra[a][3]);
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            o.blo[b] = fp8x8_to_bf16(rb[b][0], rb[b][1]);
-            o.bhi[b] = fp8x8_to_bf16(rb[b][2], rb[b][3]);
-        }
-    };
-    auto mfmas = [&](const Operands& o) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.alo[a], o.blo[b], acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.ahi[a], o.bhi[b], acc[a][b], 0, 0, 0);
-            }
+            r.b[b] = *reinterpret_cast<const u32x4*>(sx + swz(wm * 64 + b * 32 + l32, 2 * p + g));
     };
 
     // Software pipeline: the LDS reads of slice p+1 are issued before the MFMAs of slice p,
@@ -277,88 +352,209 @@ __global__ __launch_bounds__(GT) void fp8_gemm_kernel(const uint8_t* __restrict_
     load(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    u32x4 ra[4], rb[2];
-    read_slice(0, 0, ra, rb);
+    SliceRegs cur;
+    read_slice(0, 0, cur);
     for (int64_t t = 0; t < nk; ++t) {
         const int st = int(t & 1);
         if (t + 1 < nk) load((t + 1) * BK, st ^ 1);
 #pragma unroll
         for (int p = 0; p < BK / 32 - 1; ++p) {
-            u32x4 na[4], nb[2];
-            read_slice(st, p + 1, na, nb);
+            SliceRegs nxt;
+            read_slice(st, p + 1, nxt);
             Operands o;
-            convert(ra, rb, o);
-            mfmas(o);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) ra[a] = na[a];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) rb[b] = nb[b];
+            convert(cur, o);
+            mfmas(o, acc);
+            cur = nxt;
         }
         Operands o;
-        convert(ra, rb, o);
+        convert(cur, o);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < nk) read_slice(st ^ 1, 0, ra, rb);
-        mfmas(o);
+        if (t + 1 < nk) read_slice(st ^ 1, 0, cur);
+        mfmas(o, acc);
+    }
+    store_tile(acc, &smem[0][0][0], [&](int r) { const int64_t m = m0 + r; return xs[m < M ? m : M - 1]; }, ws, M, N,
+               m0, n0, y);
+}
+
+// ------------------------------------------------------------------ 3. one-launch form
+//
+// The whole cascade in one launch (the explainer's single-kernel level): each 256 x 256
+// tile first reduces the absolute maxima of its own 256 X rows (every tile of a tile row
+// repeats that reduction: there is no exchange between workgroups), then streams bf16 X
+// through LDS and quantises it there, a K step ahead of the matrix products, into the same
+// code layout the two-launch form loads. Codes and scales come from the same quantiser
+// (codes8) and the products run in the same order, so Y, the scales and the codes are
+// bit-identical to the two-launch form. The price is the X traffic: every tile reads its
+// X rows in bf16 twice (absolute maxima, then the operand), against one read of 8-bit
+// codes per tile in the two-launch form.
+constexpr int FBK = 64;                 // code bytes of K per step
+constexpr int FCODE = BT * FBK;         // 16 KiB: one operand's codes per stage
+constexpr int FSTG = BT * FBK * 2;      // 32 KiB: bf16 X of one step
+
+// Code rows of 64 bytes = 4 chunks of 16 bytes. A read group of 16 lanes takes 16
+// consecutive rows at one logical chunk: rows r..r+3 fill one 256-byte bank row, and the
+// XOR with (row >> 2) & 3 gives the four rows sharing a bank-row position four distinct
+// chunks, so the 16 reads hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * FBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+__global__ __launch_bounds__(GT) void fp8_gemm_fused_kernel(const uint16_t* __restrict__ x,
+                                                            const uint8_t* __restrict__ wq,
+                                                            const float* __restrict__ ws, int64_t M, int64_t N,
+                                                            int64_t K, int tiles_m, int tiles_n,
+                                                            uint16_t* __restrict__ y, float* __restrict__ xs_out,
+                                                            uint8_t* __restrict__ xq_out) {
+    // [0, 64 KiB): codes, stage s at s * 2 * FCODE (W, then X); [64, 128 KiB): two bf16 X
+    // staging buffers. The epilogue reuses all 128 KiB.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * FCODE + 2 * FSTG];
+    __shared__ float sig[BT], rcp[BT];
+    uint8_t* const codes = smem;
+    uint8_t* const stage = smem + 4 * FCODE;
+
+    int64_t tn, tm;
+    tile_of(blockIdx.x, int64_t(gridDim.x), tiles_m, tiles_n, tn, tm);
+    const int64_t n0 = tn * BT, m0 = tm * BT;
+    const bool owner = tn == 0;        // the tile that writes x_scale and the codes of its rows
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int wn = wave >> 2, wm = wave & 3;
+
+    // 1. Row scales. Wave w reduces rows 32w..32w+31, four rows at a time with four 16-byte
+    //    loads per row in flight per lane; rows past M get sigma = 0.
+    const int nch = int(K / 8);
+    for (int rg = 0; rg < 32; rg += 4) {
+        uint32_t am[4] = {0u, 0u, 0u, 0u};
+        const u32x4* rp[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t m = m0 + wave * 32 + rg + q;
+            rp[q] = reinterpret_cast<const u32x4*>(x + (m < M ? m : M - 1) * K);
+        }
+        for (int ch = lane; ch < nch; ch += 256) {
+            u32x4 v[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = ch + 64 * u;
+                    v[q][u] = c < nch ? rp[q][c] : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) am[q] = absmax8(v[q][u], am[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) am[q] = max(am[q], uint32_t(__shfl_xor(int(am[q]), d, 64)));
+            const int r = wave * 32 + rg + q;
+            const int64_t m = m0 + r;
+            const float sigma = m < M ? bf16_to_f32(am[q]) / 448.0f : 0.0f;   // IEEE fp32 division
+            if (lane == 0) {
+                sig[r] = sigma;
+                rcp[r] = 1.0f / sigma;                                          // inf for a zero row; unused then
+                if (owner && m < M) xs_out[m] = sigma;
+            }
+        }
     }
 
-    // acc[a][b][r] = C^T[n][m]: n = n0 + wn*128 + a*32 + (r/4)*8 + 4g + r%4, m = m0 + wm*64 + b*32 + l32.
-    // Epilogue: scale, round to bf16 and stage the wave's 64 (m) x 128 (n) block in LDS
-    // (the operand stages are free after the last barrier), then write whole rows with
-    // 16-byte stores so every output line is written once and completely.
-    uint16_t* stg = reinterpret_cast<uint16_t*>(&smem[0][0][0]) + wave * (64 * 128);
-    float wsc[4][4][4];
+    // 2. W codes by direct global -> LDS loads: 16 KiB per step, two instructions per wave,
+    //    each 16 rows x 64 bytes (lane i: row i/4, physical chunk i%4). They are issued from
+    //    inline assembly (lds_dma16): a load the compiler tracks would make it wait for the
+    //    loads into the staging buffer before every LDS read of the step. The explicit
+    //    vmcnt wait before each barrier orders them.
+    auto load_w = [&](int64_t k0, int s) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r0 = (wave * 2 + j) * 16;
+            const int r = r0 + (lane >> 2);
+            const int ch = (lane & 3) ^ ((r >> 2) & 3);
+            int64_t gr = n0 + r;
+            gr = gr < N ? gr : N - 1;
+            lds_dma16(wq + gr * K + k0 + ch * 16, &codes[s * 2 * FCODE + r0 * FBK]);
+        }
+    };
+    //    bf16 X by direct loads into a staging buffer: 32 KiB per step, four instructions per
+    //    wave, each 8 rows x 128 bytes, unswizzled.
+    auto load_x = [&](int64_t k0, int b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r0 = (wave * 4 + j) * 8;
+            const int r = r0 + (lane >> 3);
+            int64_t gr = m0 + r;
+            gr = gr < M ? gr : M - 1;
+            lds_dma16(x + gr * K + k0 + (lane & 7) * 8, &stage[b * FSTG + r0 * 128]);
+        }
+    };
+    //    Staging buffer b -> X codes of stage s: 2048 chunks of 8 values, four per thread;
+    //    a wave reads 1 KiB of consecutive chunks and writes 8-byte code pairs.
+    auto quantize = [&](int64_t k0, int b, int s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = j * GT + tid;
+            const int r = idx >> 3, c = idx & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[b * FSTG + r * 128 + c * 16]);
+            const uint2 q = codes8(v, sig[r], rcp[r]);
+            *reinterpret_cast<uint2*>(&codes[s * 2 * FCODE + FCODE + swz64(r, c >> 1) + 8 * (c & 1)]) = q;
+            if (owner && xq_out != nullptr && m0 + r < M)
+                *reinterpret_cast<uint2*>(xq_out + (m0 + r) * K + k0 + c * 8) = q;
+        }
+    };
+    auto read_slice = [&](int s, int p, SliceRegs& rr) {
+        const uint8_t* sw = codes + s * 2 * FCODE;
+        const uint8_t* sx = sw + FCODE;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            rr.a[a] = *reinterpret_cast<const u32x4*>(sw + swz64(wn * 128 + a * 32 + l32, 2 * p + g));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            rr.b[b] = *reinterpret_cast<const u32x4*>(sx + swz64(wm * 64 + b * 32 + l32, 2 * p + g));
+    };
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                int64_t n = n0 + wn * 128 + a * 32 + q4 * 8 + 4 * g + e;
-                n = n < N ? n : N - 1;
-                wsc[a][q4][e] = ws[n];
-            }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        int64_t m = m0 + wm * 64 + b * 32 + l32;
-        const float sx = xs[m < M ? m : M - 1];
-        const int ml = b * 32 + l32;           // row of the staging block
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int nl = a * 32 + q4 * 8 + 4 * g;   // column of the staging block (multiple of 4)
-                const f32x16& c = acc[a][b];
-                const uint2 w2 = make_uint2(
-                    pack_bf16x2((c[4 * q4 + 0] * sx) * wsc[a][q4][0], (c[4 * q4 + 1] * sx) * wsc[a][q4][1]),
-                    pack_bf16x2((c[4 * q4 + 2] * sx) * wsc[a][q4][2], (c[4 * q4 + 3] * sx) * wsc[a][q4][3]));
-                // 16-byte chunks of a staging row are rotated by the row index to spread banks.
-                const int chunk = ((nl >> 3) + ml) & 15;
-                *reinterpret_cast<uint2*>(stg + ml * 128 + chunk * 8 + (nl & 7)) = w2;
-            }
-    }
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+    // 3. Pipeline. At the top of step t the codes of stage t&1 are complete and staging
+    //    buffer (t+1)&1 holds bf16 X of step t+1. Step t loads W of step t+1 into the other
+    //    code stage and bf16 X of step t+2 into staging buffer t&1 (quantised during step
+    //    t-1), quantises staging buffer (t+1)&1 into the other code stage, and multiplies
+    //    the two 32-byte slices of stage t&1.
+    const int64_t nk = K / FBK;
+    load_w(0, 0);
+    load_x(0, 0);
+    if (nk > 1) load_x(FBK, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                   // also publishes sig / rcp
+    quantize(0, 0, 0);
     __syncthreads();
-    // 64 rows x 16 chunks of 16 bytes: each instruction writes 4 whole rows.
-    const int64_t nbase = n0 + wn * 128;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int ml = it * 4 + (lane >> 4);
-        const int ch = lane & 15;
-        const int64_t m = m0 + wm * 64 + ml;
-        const int64_t n = nbase + ch * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + ml * 128 + (((ch + ml) & 15) * 8));
-        if (m < M) {
-            uint16_t* dst = y + m * N + n;
-            if (n + 7 < N && ((N & 7) == 0)) {
-                *reinterpret_cast<u32x4*>(dst) = v;
-            } else {
-                const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (n + e < N) dst[e] = hv[e];
-            }
+    SliceRegs cur;
+    read_slice(0, 0, cur);
+    for (int64_t t = 0; t < nk; ++t) {
+        const int st = int(t & 1);
+        if (t + 1 < nk) load_w((t + 1) * FBK, st ^ 1);
+        if (t + 2 < nk) load_x((t + 2) * FBK, st);
+        {
+            SliceRegs nxt;
+            read_slice(st, 1, nxt);
+            Operands o;
+            convert(cur, o);
+            mfmas(o, acc);
+            cur = nxt;
         }
+        if (t + 1 < nk) quantize((t + 1) * FBK, st ^ 1, st ^ 1);
+        Operands o;
+        convert(cur, o);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < nk) read_slice(st ^ 1, 0, cur);
+        mfmas(o, acc);
     }
+    store_tile(acc, smem, [&](int r) { return sig[r]; }, ws, M, N, m0, n0, y);
 }
 
 }  // namespace
@@ -374,6 +570,16 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* c
     else if (nct <= 8) hipLaunchKernelGGL(quant_rows_kernel<8>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
     else if (nct <= 16) hipLaunchKernelGGL(quant_rows_kernel<16>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
     else hipLaunchKernelGGL(quant_rows_kernel<0>, grid, dim3(QT), 0, stream, x, M, K, codes, x_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_gemm_fused(const uint16_t* x, const uint8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                                   int64_t K, uint16_t* y, float* x_scale, uint8_t* xq, hipStream_t stream) {
+    const int64_t tm = ceil_div(M, BT), tn = ceil_div(N, BT);
+    const int64_t blocks = tm * tn;
+    if (blocks > INT32_MAX || K % FBK != 0 || K / 8 > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_gemm_fused_kernel, dim3(unsigned(blocks)), dim3(GT), 0, stream, x, wq, w_scale, M, N, K,
+                       int(tm), int(tn), y, x_scale, xq);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 4
+#define RF_ABI_VERSION 5
 
 /* Exported symbols (the library is built with hidden visibility by default). */
 #if defined(__GNUC__) || defined(__clang__)
@@ -420,6 +420,27 @@ RF_API size_t rf_quant_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 RF_API rf_status rf_quant_gemm(const void* x, const uint8_t* wq, const float* w_scale, int64_t M,
                         int64_t N, int64_t K, void* y, float* x_scale, uint8_t* xq,
                         void* workspace, size_t ws_bytes, rf_stream stream);
+
+/*
+ * rf_quant_gemm_fused -- the same cascade as rf_quant_gemm in ONE launch (the
+ * explainer's single-kernel fusion level, section 3.3, applied to the
+ * quantisation cascade of section 4.3), with no workspace.
+ *
+ * Each 256 x 256 output tile reduces the absolute maxima of its own 256 rows of
+ * X, then quantises bf16 X into LDS a K step ahead of the matrix products. No
+ * workgroup waits for another, so the maxima are recomputed by every tile of a
+ * row of tiles, and X is read in bf16 by every tile instead of once as codes.
+ * The explainer's section 6 warns that fusion can lose to the unfused form; this
+ * form exists to measure that (rf_quant_gemm is the faster one on the workloads
+ * measured here). y, x_scale and xq are bit-identical to rf_quant_gemm's.
+ *
+ *   Arguments, layouts and limits as rf_quant_gemm; xq [M, K] may be NULL (the
+ *   codes are then not stored anywhere). Outputs must not alias the inputs or
+ *   each other (RF_ERR_INVALID_ARGUMENT).
+ */
+RF_API rf_status rf_quant_gemm_fused(const void* x, const uint8_t* wq, const float* w_scale, int64_t M,
+                              int64_t N, int64_t K, void* y, float* x_scale, uint8_t* xq,
+                              rf_stream stream);
 
 #ifdef __cplusplus
 }

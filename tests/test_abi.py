@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "rf_cascade_gemm",
         "rf_attn_decode_workspace_size", "rf_attn_decode", "rf_attn_decode_noalloc",
         "rf_moe_route", "rf_moe_route_split_workspace_size", "rf_moe_route_split",
-        "rf_quant_gemm_workspace_size", "rf_quant_gemm"])
+        "rf_quant_gemm_workspace_size", "rf_quant_gemm", "rf_quant_gemm_fused"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rf_abi_version() == 4
+    assert lib.rf_abi_version() == 5
     for code, name in [(0, b"RF_OK"), (1, b"RF_ERR_INVALID_ARGUMENT"), (2, b"RF_ERR_UNSUPPORTED"),
                        (3, b"RF_ERR_BUFFER_TOO_SMALL"), (4, b"RF_ERR_DEVICE")]:
         assert lib.rf_status_string(code) == name
@@ -149,6 +149,23 @@ def test_quant_gemm_validation(lib):
     assert _qg(lib, xq=None, work=P6, nbytes=16 * 256 - 1) == TOO_SMALL
     assert _qg(lib, y=P) == INVALID
     assert _qg(lib, xq=P4 + 16) == INVALID
+
+
+def _qgf(lib, x=P, wq=P2, ws=P3, M=16, N=16, K=256, y=P4, xs=P5, xq=P6):
+    return lib.rf_quant_gemm_fused(x, wq, ws, M, N, K, y, xs, xq, None)
+
+
+def test_quant_gemm_fused_validation(lib):
+    assert _qgf(lib, x=None) == INVALID
+    assert _qgf(lib, ws=None) == INVALID
+    assert _qgf(lib, xs=None) == INVALID
+    assert _qgf(lib, K=100) == UNSUPPORTED
+    assert _qgf(lib, K=64) == UNSUPPORTED
+    assert _qgf(lib, N=0) == INVALID
+    assert _qgf(lib, y=P) == INVALID                        # y aliases x
+    assert _qgf(lib, xq=P4 + 16) == INVALID                 # codes inside y
+    assert _qgf(lib, xs=P6 + 8) == INVALID                  # x_scale inside the codes
+    assert _qgf(lib, M=1 << 21, K=1 << 20) == UNSUPPORTED   # M*K beyond 2^40
 
 
 def test_binding_rejects_cpu_tensors():
