@@ -11,10 +11,10 @@
 // G(x) (x) H(d1) all come from Cascade<Spec>; the last reduction, a contraction with W,
 // runs on v_mfma_f32_32x32x16_bf16 with each weight split into two bf16 parts.
 //
-// gfx950 mapping: a workgroup of 4 waves owns 128 rows (32 per wave) and walks K in
-// chunks of 32. Each chunk's W slice [32 x N] bf16 and the wave's X slice [32 x 32] fp32
-// go to LDS by direct global-to-LDS loads issued two chunks ahead (3-slot rings), so no
-// registers hold data in flight. The output is formed as Y^T = W^T P^T (as the attention
+// gfx950 mapping: a workgroup of 4 waves owns 128 rows (32 per wave) and walks K in chunks
+// of 32. Each chunk's W slice [32 x N] bf16 and each wave's X slice [32 x 32] fp32 go to LDS
+// by direct global-to-LDS loads issued two chunks ahead (3-slot rings), so no registers
+// hold data in flight. The output is formed as Y^T = W^T P^T (as the attention
 // kernels form O^T = V^T P^T): W^T comes from LDS through the transposing read
 // (ds_read_b64_tr_b16) and P^T is the packed weights as each lane computes them, so every
 // lane owns one row and the lead's correction is a per-lane scale.
@@ -37,7 +37,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
 
 constexpr int KC = 32;         // K per chunk
-constexpr int ROWS = 128;      // rows per workgroup (32 per wave)
+constexpr int NW = 4;           // waves per workgroup
+constexpr int ROWS = 32 * NW;   // rows per workgroup (32 per wave)
 constexpr int STAGES = 3;
 constexpr int XSLOT = ROWS * KC * 4;   // bytes of X per stage (16 KiB)
 
@@ -58,7 +59,7 @@ __device__ __forceinline__ int x_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int x_piece(int row, int piece) { return row * 8 + (piece ^ x_swz(row)); }
 
 template <class Spec, int N>
-__global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __restrict__ x,
+__global__ __launch_bounds__(NW * 64, 2) void cascade_gemm_kernel(const float* __restrict__ x,
                                                               const uint16_t* __restrict__ w, int64_t M, int64_t K,
                                                               float xscale, float* __restrict__ y,
                                                               float* __restrict__ stat) {
@@ -69,10 +70,10 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
     constexpr int RPW = 64 / CH;              // W rows per wave load
     constexpr int WSLOT = KC * N * 2;         // bytes of W per stage
     constexpr int WL = WSLOT / 1024;          // wave loads per W slice
-    constexpr int WPW = WL / 4;               // ... per wave
+    constexpr int WPW = WL / NW;              // ... per wave
     constexpr int DB = N / 32;                // 32-wide output blocks
     constexpr int LPC = 4 + WPW;              // direct loads per wave per chunk
-    static_assert(WPW >= 1 && WL % 4 == 0, "every wave loads a share of the W slice");
+    static_assert(WPW >= 1 && WL % NW == 0, "every wave loads a share of the W slice");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * (XSLOT + WSLOT)];
     unsigned char* const xring = smem;                       // [stage][wave][32 rows x 128 B]
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t row0 = int64_t(blockIdx.x) * ROWS + 32 * wave;   // first row of this wave
     const int64_t row = row0 + l32;
-    const int nchunks = int((K + KC - 1) / KC);
+    const int K32 = int(K);                   // the host bounds K below 2^24
+    const int nchunks = (K32 + KC - 1) / KC;
 
     // ---- direct loads. X: wave load l of a chunk covers the wave's rows 8l .. 8l + 7 (lane i:
     // row 8l + i/8, physical piece i%8, fetching the logical piece that maps there). Rows past M
@@ -116,20 +118,26 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
     }
     auto issue = [&](int t) {
         const int st = t % STAGES;
-        const int64_t k0 = int64_t(t < nchunks ? t : nchunks - 1) * KC;
+        const int k0 = (t < nchunks ? t : nchunks - 1) * KC;
         const uint32_t xl = xl_base + uint32_t(st * XSLOT);
+        const unsigned char* wl = reinterpret_cast<const unsigned char*>(wring) + st * WSLOT + wave * WPW * 1024;
+        if (k0 + KC <= K32) {                 // the whole chunk lies inside K (wave-uniform)
 #pragma unroll
-        for (int l = 0; l < 4; ++l) {
-            const int64_t k = k0 + x_piece_k[l];
-            const uint32_t off = x_src[l] + uint32_t((k < K ? k : 0) * 4);
-            lds_dma16_sb(xw, off, xl + uint32_t(l * 1024));
-        }
+            for (int l = 0; l < 4; ++l) lds_dma16_sb(xw, x_src[l] + uint32_t((k0 + x_piece_k[l]) * 4), xl + l * 1024);
 #pragma unroll
-        for (int l = 0; l < WPW; ++l) {
-            const int r = (wave * WPW + l) * RPW + lane / CH;
-            const int64_t kr = k0 + r < K ? k0 + r : K - 1;   // rows past K re-read row K - 1
-            lds_dma16(w + kr * N + (w_off[l] - r * N), reinterpret_cast<const unsigned char*>(wring) + st * WSLOT +
-                                                          (wave * WPW + l) * 1024);
+            for (int l = 0; l < WPW; ++l) lds_dma16(w + int64_t(k0) * N + w_off[l], wl + l * 1024);
+        } else {
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const int k = k0 + x_piece_k[l];
+                lds_dma16_sb(xw, x_src[l] + uint32_t((k < K32 ? k : 0) * 4), xl + l * 1024);
+            }
+#pragma unroll
+            for (int l = 0; l < WPW; ++l) {
+                const int r = (wave * WPW + l) * RPW + lane / CH;
+                const int kr = k0 + r < K32 ? k0 + r : K32 - 1;   // rows past K re-read row K - 1
+                lds_dma16(w + int64_t(kr) * N + (w_off[l] - r * N), wl + l * 1024);
+            }
         }
     };
 
@@ -173,11 +181,14 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
         for (int c = 0; c < 4; ++c) {
             const fx4 v = *reinterpret_cast<const fx4*>(xs + x_piece(l32, 2 * c + h) * 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = t * KC + 8 * c + 4 * h + e;
-                const float val = v[e] * xscale;
-                xv[4 * c + e] = k < K ? val : (SOFTMAX ? kNegInf : 0.f);
-            }
+            for (int e = 0; e < 4; ++e) xv[4 * c + e] = v[e] * xscale;
+        }
+        if ((t + 1) * KC > K32) {             // the last chunk runs past K (wave-uniform): null entries
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t * KC + 8 * c + 4 * h + e >= K32) xv[4 * c + e] = SOFTMAX ? kNegInf : 0.f;
         }
         // The lead over this chunk: the lane's 16 values, then its partner lane (l ^ 32).
         Lead tl = lead;
@@ -201,19 +212,30 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
         // bf16 tail (p = head + tail to about 2^-17 relative), so the contraction on the bf16
         // matrix cores loses no more than fp32 accumulation does; the row sum reads the same
         // two parts, so numerator and denominator see identical weights.
+        // A null entry's term is exactly 0 against any lead but the identity (which only a row
+        // with nothing but null entries so far still holds), so the entries are tested only
+        // when some lane of the wave still has the identity lead.
         uint32_t ph[8], pt[8];
+        auto weights = [&](auto test_null) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float a = xv[2 * i], b = xv[2 * i + 1];
-            const float pa = Spec::is_null(a) ? 0.f : Spec::weight(C::term(a, lead));
-            const float pb = Spec::is_null(b) ? 0.f : Spec::weight(C::term(b, lead));
-            ph[i] = pack_bf16(pa, pb);
-            pt[i] = pack_bf16(pa - bf16_lo(ph[i]), pb - bf16_hi(ph[i]));
-            if constexpr (SOFTMAX) {
-                s_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ph[i]), ones, s_part, false);
-                s_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pt[i]), ones, s_part, false);
+            for (int i = 0; i < 8; ++i) {
+                const float a = xv[2 * i], b = xv[2 * i + 1];
+                float pa = Spec::weight(C::term(a, lead));
+                float pb = Spec::weight(C::term(b, lead));
+                if constexpr (decltype(test_null)::value) {
+                    pa = Spec::is_null(a) ? 0.f : pa;
+                    pb = Spec::is_null(b) ? 0.f : pb;
+                }
+                ph[i] = pack_bf16(pa, pb);
+                pt[i] = pack_bf16(pa - bf16_lo(ph[i]), pb - bf16_hi(ph[i]));
+                if constexpr (SOFTMAX) {
+                    s_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ph[i]), ones, s_part, false);
+                    s_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pt[i]), ones, s_part, false);
+                }
             }
-        }
+        };
+        if (__any(Spec::lead_is_identity(lead))) weights(std::true_type{});
+        else weights(std::false_type{});
         // Y^T += W^T (P_head + P_tail)^T over the chunk's two 16-wide K slices.
         const uint16_t* ws = wring + st * (WSLOT / 2);
 #pragma unroll
@@ -259,9 +281,9 @@ __global__ __launch_bounds__(256, 2) void cascade_gemm_kernel(const float* __res
 template <class Spec, int N>
 hipError_t launch_n(const float* x, const uint16_t* w, int64_t M, int64_t K, float xscale, float* y, float* stat,
                     hipStream_t stream) {
-    const int64_t blocks = ceil_div(M, ROWS);
+    const int64_t blocks = ceil_div(M, int64_t(ROWS));
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((cascade_gemm_kernel<Spec, N>), dim3(unsigned(blocks)), dim3(256), 0, stream, x, w, M, K,
+    hipLaunchKernelGGL((cascade_gemm_kernel<Spec, N>), dim3(unsigned(blocks)), dim3(NW * 64), 0, stream, x, w, M, K,
                        xscale, y, stat);
     return hipGetLastError();
 }
