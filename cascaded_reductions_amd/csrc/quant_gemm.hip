@@ -4,9 +4,12 @@
 // section 4.3: scale = max|X| / 448 per row, codes = round(X / scale) to OCP
 // E4M3FN, then Y = codes . W dequantised by the row and column scales. The
 // scale needs the whole row's maximum before any code can be formed, and
-// rounding has no incremental form (its inverse does not exist), so the cascade
-// runs as two launches on one stream (the explainer's multi-kernel level,
-// section 3.3):
+// rounding has no incremental form (its inverse does not exist). The cascade is
+// built in two forms with identical results: two launches on one stream (the
+// explainer's multi-kernel level, section 3.3; the faster form, parts 1 and 2
+// below), and one launch (section 4.3's full fusion; part 3) in which every
+// output tile reduces its own rows' maxima and quantises X in LDS. The two-launch
+// form:
 //  1. quant_rows: one wave per row keeps the row in registers, reduces the
 //     absolute maximum (an integer max over the bf16 magnitude bits), forms
 //     sigma = a / 448 and each code from the IEEE fp32 quotient x / sigma
