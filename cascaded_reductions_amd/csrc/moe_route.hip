@@ -6,21 +6,23 @@
 //
 // Each workgroup owns TB = 8 tokens and all E experts, so no workgroup depends on
 // another (no partial scores leave the chip and no second launch is needed):
-//  * its 4 waves split the hidden axis into contiguous quarters and stream their quarter
-//    of W_gate ([32 hidden x E] bf16 chunks) and of the 8 tokens' X through wave-private
-//    LDS rings filled by direct global-to-LDS loads, 6 chunks ahead, so every wave runs
-//    without barriers until the end;
+//  * its NW waves (8 up to E = 64, 4 above) split the hidden axis into contiguous shares
+//    and stream their share of W_gate ([32 hidden x E] bf16 chunks) and of the 8 tokens'
+//    X through wave-private LDS rings filled by direct global-to-LDS loads a few chunks
+//    ahead (none past the end of the share), so every wave runs without barriers until
+//    the end; two waves per SIMD keep one wave's loads in flight while the other computes;
 //  * the gate GEMM runs on v_mfma_f32_16x16x32_bf16 with the tokens as the M dimension
 //    (8 of 16 rows used) and W entering through the transposing LDS read, so the [Hd, E]
 //    layout needs no transpose in memory;
-//  * the 4 waves' partial scores are added through LDS in a fixed order (deterministic),
+//  * the waves' partial scores are added through LDS in a fixed order (deterministic),
 //    then sixteen lanes per token keep sorted top-k lists over a sixteenth of the experts,
-//    merged by four cross-lane steps, and the first lane applies the softmax over the k.
+//    merged by four DPP steps (moe_topk.hpp), and the first lane applies the softmax.
 // Every workgroup reads the whole W_gate (E * Hd * 2 bytes, 0.5 MiB at 4096 x 64) from its
 // XCD's L2 and X once; the per-CU rate of those L2 reads bounds the kernel (the two-launch
 // form in moe_route_split.hip reads a range of W per CU instead, and exchanges partials).
 #include "common.hpp"
 #include "launch.hpp"
+#include "moe_topk.hpp"
 
 namespace rf {
 namespace {
@@ -29,70 +31,71 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int TB = 8;                 // tokens per workgroup
-constexpr int NWAVE = 4;
-constexpr int WAVE_LDS = 36 * 1024;   // LDS ring bytes per wave
+
+// Waves per workgroup: two per SIMD while a wave's ring (20 KiB of LDS) still holds a
+// chunk pair in flight beside the one being used, one per SIMD (36 KiB rings) above.
+constexpr int waves_for(int E) { return E <= 64 ? 8 : 4; }
 
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
 }
 
-// (s1, i1) ranks before (s2, i2).
-__device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
-    return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
-// Insert (s, i) into the sorted list (ts, ti) of length K (descending rank).
-template <int K>
-__device__ __forceinline__ void topk_insert(float (&ts)[K], int (&ti)[K], float s, int i) {
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-        if (better(s, i, ts[r], ti[r])) {
-            const float s2 = ts[r];
-            const int i2 = ti[r];
-            ts[r] = s;
-            ti[r] = i;
-            s = s2;
-            i = i2;
-        }
-    }
-}
-
 // Ring geometry for E experts: a W chunk is 32 hidden rows x E bf16 (E / 16 KiB), an X
-// chunk pair is the 8 tokens x 64 hidden values (1 KiB). DEPTH chunk slots per wave.
+// chunk pair is the 8 tokens x 64 hidden values (1 KiB). DEPTH chunk slots per wave, of
+// which DEPTH / 2 - 1 pairs are in flight ahead of the pair in use.
 template <int NEB>
 struct Ring {
     static constexpr int E = NEB * 16;
+    static constexpr int NW = waves_for(E);
+    static constexpr int WAVE_LDS = NW == 8 ? 20 * 1024 : 36 * 1024;
     static constexpr int WCH = 64 * E;                       // bytes of one W chunk
     static constexpr int WLOADS = WCH / 1024;                // wave loads per W chunk
     static constexpr int DEPTH0 = (WAVE_LDS - 4096) / WCH;   // W slots that fit beside the X slots
     static constexpr int DEPTH = DEPTH0 >= 8 ? 8 : DEPTH0 >= 4 ? 4 : 2;   // power of two
     static constexpr int XPAIRS = DEPTH / 2;                 // X slots (one per chunk pair)
+    static constexpr int AHEAD = DEPTH / 2 - 1;
     static_assert(DEPTH * WCH + XPAIRS * 1024 <= WAVE_LDS, "the wave's ring must fit its LDS share");
+    static_assert(NW * WAVE_LDS <= 160 * 1024, "the rings must fit the CU's LDS");
+    static constexpr int PSTRIDE = E + 16;                   // floats per partial-score row
+    static_assert(NW * TB * PSTRIDE * 4 <= NW * WAVE_LDS, "the partial scores reuse the rings");
 };
 
+// Wait until the loads of the pair in use have landed, with `left` more pairs of this wave
+// issued after it (left >= N: N pairs; the wait count must be an immediate).
+template <int N, int LPS>
+__device__ __forceinline__ void wait_pairs(int left) {
+    if constexpr (N == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (left >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * LPS) : "memory");
+        else wait_pairs<N - 1, LPS>(left);
+    }
+}
+
 template <int NEB, int K>
-__global__ __launch_bounds__(NWAVE * 64) void moe_gate_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(Ring<NEB>::NW * 64) void moe_gate_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ wg, int64_t T,
                                                               int64_t Hd, int k, int swz, int32_t* __restrict__ idx,
                                                               float* __restrict__ wout, float* __restrict__ scores) {
     using R = Ring<NEB>;
     constexpr int E = R::E;
+    constexpr int NW = R::NW;
     constexpr int DEPTH = R::DEPTH;
     constexpr int LPS = 2 * R::WLOADS + 1;    // direct loads per chunk pair (two W chunks + one X pair)
-    __shared__ __attribute__((aligned(16))) unsigned char smem[NWAVE * WAVE_LDS];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NW * R::WAVE_LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int64_t t0 = int64_t(blockIdx.x) * TB;
 
-    unsigned char* const ring = smem + wave * WAVE_LDS;
+    unsigned char* const ring = smem + wave * R::WAVE_LDS;
     unsigned char* const wslots = ring;                       // DEPTH x WCH
     unsigned char* const xslots = ring + DEPTH * R::WCH;      // XPAIRS x 1 KiB
 
     // This wave's contiguous share of the hidden axis, in 32-wide chunks, taken in pairs.
     const int64_t nch = Hd / 32;
-    const int64_t per = (nch + NWAVE - 1) / NWAVE;
+    const int64_t per = (nch + NW - 1) / NW;
     const int64_t c_begin = wave * per < nch ? wave * per : nch;
     const int64_t c_end = c_begin + per < nch ? c_begin + per : nch;
     const int my = int(c_end - c_begin);      // chunks of this wave (wave-uniform)
@@ -119,9 +122,8 @@ __global__ __launch_bounds__(NWAVE * 64) void moe_gate_kernel(const uint16_t* __
         const int lc = pc ^ (((row & 3) << 1) & swz);
         w_lane[l] = uint32_t(row * E * 2 + lc * 16);
     }
-    auto issue_pair = [&](int p) {            // chunks 2p and 2p + 1 of this wave (npairs >= 1)
-        const int pc = p < npairs ? p : npairs - 1;
-        const int64_t c0 = c_begin + 2 * pc;
+    auto issue_pair = [&](int p) {            // chunks 2p and 2p + 1 of this wave (p < npairs)
+        const int64_t c0 = c_begin + 2 * p;
         const uint32_t xs = lds_addr(xslots) + uint32_t((p % R::XPAIRS) * 1024);
         // A pair whose second chunk is past the hidden axis (an odd chunk count) fetches the
         // first chunk's pieces in its place (unused), so no load runs past the end of X.
@@ -158,15 +160,15 @@ __global__ __launch_bounds__(NWAVE * 64) void moe_gate_kernel(const uint16_t* __
     const int at = l16 & 7;
     const int a_off[2] = {at * 128 + ((((0 + g) ^ at) & 7) * 16), at * 128 + ((((4 + g) ^ at) & 7) * 16)};
 
-    // Prologue: DEPTH / 2 - 1 pairs in flight. (A wave with no chunks, when the hidden axis is
-    // shorter than 4 chunks, loads nothing and contributes zeros.)
-    if (npairs > 0) {
+    // Prologue: up to AHEAD pairs in flight. No load is issued past the wave's last pair, so
+    // the last AHEAD waits count fewer pairs. (A wave with no chunks, when the hidden axis has
+    // fewer chunks than waves, loads nothing and contributes zeros.)
 #pragma unroll
-        for (int p = 0; p < DEPTH / 2 - 1; ++p) issue_pair(p);
-    }
+    for (int p = 0; p < R::AHEAD; ++p)
+        if (p < npairs) issue_pair(p);
     for (int p = 0; p < npairs; ++p) {
-        issue_pair(p + DEPTH / 2 - 1);        // into the slots pair p - 1 used (read last iteration)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH / 2 - 1) * LPS) : "memory");   // pair p is in
+        if (p + R::AHEAD < npairs) issue_pair(p + R::AHEAD);   // into the slots pair p - 1 used
+        wait_pairs<R::AHEAD, LPS>(npairs - 1 - p);             // pair p is in
         const unsigned char* xs = xslots + (p % R::XPAIRS) * 1024;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -184,74 +186,42 @@ __global__ __launch_bounds__(NWAVE * 64) void moe_gate_kernel(const uint16_t* __
             }
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // retire the trailing (unused) loads
 
     // acc[b][r] = partial score of token 4g + r (g < 2: tokens 0..7) for expert 16b + l16. The
-    // waves' partials meet in LDS ([wave][token][expert] fp32; the rings are free after the
+    // waves' partials meet in LDS ([wave][token][expert] fp32, rows padded to E + 16 floats so
+    // the four tokens a wave reads below sit in different banks; the rings are free after the
     // barrier) and are added in wave order.
+    constexpr int PS = R::PSTRIDE;
     __syncthreads();
     float* part = reinterpret_cast<float*>(smem);
     if (g < 2) {
 #pragma unroll
         for (int b = 0; b < NEB; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[(wave * TB + 4 * g + r) * E + 16 * b + l16] = acc[b][r];
+            for (int r = 0; r < 4; ++r) part[(wave * TB + 4 * g + r) * PS + 16 * b + l16] = acc[b][r];
     }
     __syncthreads();
 
-    // Sixteen lanes per token (waves 0 and 1: 128 threads for 8 tokens); lane q of a token owns
-    // experts q * NEB .. q * NEB + NEB - 1.
+    // Sixteen lanes per token, one DPP row each (waves 0 and 1: 128 threads for 8 tokens); lane
+    // q of a token owns experts q, q + 16, ..., q + 16 (NEB - 1).
     if (tid >= TB * 16) return;               // whole waves only: no barrier follows
     const int tok = tid >> 4, q = tid & 15;
     const int64_t t_out = t0 + tok;
-    float ts[K];
-    int ti[K];
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-        ts[r] = kNegInf;
-        ti[r] = 0x7FFFFFFF;
-    }
+    uint64_t list[K];
+    moe::clear<K>(list);
 #pragma unroll
     for (int e = 0; e < NEB; ++e) {
-        const int ex = q * NEB + e;
-        float s = part[tok * E + ex];
+        const int ex = 16 * e + q;
+        float s = part[tok * PS + ex];
 #pragma unroll
-        for (int w = 1; w < NWAVE; ++w) s += part[(w * TB + tok) * E + ex];
+        for (int w = 1; w < NW; ++w) s += part[(w * TB + tok) * PS + ex];
         if (scores && t_out < T) scores[t_out * E + ex] = s;
-        topk_insert<K>(ts, ti, s, ex);
+        moe::insert<K>(list, moe::make_key(s, ex));
     }
-    // Merge the sixteen lanes' lists of a token (lanes differing in bits 0-3).
-#pragma unroll
-    for (int mask = 1; mask <= 8; mask <<= 1) {
-        float os[K];
-        int oi[K];
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            os[r] = __shfl_xor(ts[r], mask, 64);
-            oi[r] = __shfl_xor(ti[r], mask, 64);
-        }
-#pragma unroll
-        for (int r = 0; r < K; ++r) topk_insert<K>(ts, ti, os[r], oi[r]);
-    }
-    // The list holds the K best; the first k (k <= K) are the output, and the softmax runs over
-    // exactly those k scores.
-    if (t_out < T && q == 0) {
-        float den = 0.f;
-        float ex[K];
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            ex[r] = r < k ? __expf(ts[r] - ts[0]) : 0.f;
-            den += ex[r];
-        }
-        const float inv = 1.f / den;
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            if (r < k) {
-                idx[t_out * k + r] = ti[r];
-                wout[t_out * k + r] = ex[r] * inv;
-            }
-        }
-    }
+    moe::merge_row16<K>(list);
+    // Every lane of the row now holds the K best; the first k (k <= K) are the output, and the
+    // softmax runs over exactly those k scores.
+    if (t_out < T && q == 0) moe::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
 }
 
 template <int NEB>
@@ -260,10 +230,10 @@ hipError_t launch_e(int k, int swz, hipStream_t stream, const uint16_t* x, const
     const dim3 grid{unsigned(ceil_div(T, TB)), 1u, 1u};
     // A top-2 fast path; any other k up to 8 keeps an 8-entry list.
     if (k == 2)
-        hipLaunchKernelGGL((moe_gate_kernel<NEB, 2>), grid, dim3(NWAVE * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
+        hipLaunchKernelGGL((moe_gate_kernel<NEB, 2>), grid, dim3(Ring<NEB>::NW * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
                            scores);
     else
-        hipLaunchKernelGGL((moe_gate_kernel<NEB, 8>), grid, dim3(NWAVE * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
+        hipLaunchKernelGGL((moe_gate_kernel<NEB, 8>), grid, dim3(Ring<NEB>::NW * 64), 0, stream, x, w, T, Hd, k, swz, idx, wout,
                            scores);
     return hipGetLastError();
 }

@@ -12,7 +12,7 @@
 //  * a second launch adds each token's range partials in range order -- a fixed order, so
 //    results are deterministic -- and runs the top-k and the softmax in registers: sixteen
 //    lanes per token each keep a sorted top-k list over a sixteenth of the experts, merged
-//    with four cross-lane steps.
+//    with four DPP steps (moe_topk.hpp).
 // Each CU reads only its range of W (64 KiB at 4096 x 64) instead of all of it, at the cost
 // of the partial scores' round trip (4 MiB at 2048 tokens) and a second launch; the kernel
 // boundary orders the two phases (the explainer's multi-kernel level, section 3.3).
@@ -21,6 +21,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "moe_topk.hpp"
 
 namespace rf {
 namespace {
@@ -52,27 +53,6 @@ MoeGeom moe_geom(int64_t T, int64_t Hd, int64_t E) {
 
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
-}
-
-// (s1, i1) ranks before (s2, i2).
-__device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
-    return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
-// Insert (s, i) into the sorted list (ts, ti) of length K (descending rank).
-template <int K>
-__device__ __forceinline__ void topk_insert(float (&ts)[K], int (&ti)[K], float s, int i) {
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-        if (better(s, i, ts[r], ti[r])) {
-            const float s2 = ts[r];
-            const int i2 = ti[r];
-            ts[r] = s;
-            ti[r] = i;
-            s = s2;
-            i = i2;
-        }
-    }
 }
 
 // Phase 1: partial scores of 64 tokens over one hidden range.
@@ -205,13 +185,8 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
     const int q = tid & 15;
     const int64_t t_out = int64_t(blockIdx.x) * (RED_T / 16) + (tid >> 4);
     const bool valid = t_out < T;
-    float ts[K];
-    int ti[K];
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-        ts[r] = kNegInf;
-        ti[r] = 0x7FFFFFFF;
-    }
+    uint64_t list[K];
+    moe::clear<K>(list);
     if (valid) {
         // Sum the range partials in range order (deterministic), loading RB ranges' worth
         // of this lane's experts before adding, so the loads overlap.
@@ -238,41 +213,14 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
 #pragma unroll
         for (int e = 0; e < NEB; ++e) {
             if (scores) scores[t_out * E + q * NEB + e] = sum[e];
-            topk_insert<K>(ts, ti, sum[e], q * NEB + e);
+            moe::insert<K>(list, moe::make_key(sum[e], q * NEB + e));
         }
     }
-    // Merge the sixteen lanes' lists of a token (lanes differing in bits 0-3).
-#pragma unroll
-    for (int mask = 1; mask <= 8; mask <<= 1) {
-        float os[K];
-        int oi[K];
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            os[r] = __shfl_xor(ts[r], mask, 64);
-            oi[r] = __shfl_xor(ti[r], mask, 64);
-        }
-#pragma unroll
-        for (int r = 0; r < K; ++r) topk_insert<K>(ts, ti, os[r], oi[r]);
-    }
-    // The list holds the K best; the first k (k <= K) are the output, and the
-    // softmax runs over exactly those k scores.
-    if (valid && q == 0) {
-        float den = 0.f;
-        float ex[K];
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            ex[r] = r < k ? __expf(ts[r] - ts[0]) : 0.f;
-            den += ex[r];
-        }
-        const float inv = 1.f / den;
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            if (r < k) {
-                idx[t_out * k + r] = ti[r];
-                wout[t_out * k + r] = ex[r] * inv;
-            }
-        }
-    }
+    // Merge the sixteen lanes' lists of a token (one DPP row; a row is wholly valid or not).
+    moe::merge_row16<K>(list);
+    // Every lane of the row now holds the K best; the first k (k <= K) are the output, and
+    // the softmax runs over exactly those k scores.
+    if (valid && q == 0) moe::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
 }
 
 template <int NEB>
