@@ -46,12 +46,24 @@
 // (+) of the last level, a contraction with a weight matrix, to the MFMA units.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
+#include "topk.hpp"
 
 namespace rf {
 namespace cascade {
 
 // ---------------------------------------------------------------- the engine
+
+// Whether a spec folds four elements at once (lead_plus4); only specs without a dependent
+// level (no running values, no payload) give it.
+template <class S, class = void>
+struct has_plus4 : std::false_type {};
+template <class S>
+struct has_plus4<S, std::void_t<decltype(&S::lead_plus4)>> : std::true_type {
+    static_assert(S::kPayload == 0, "lead_plus4 is for cascades without a payload");
+};
 
 template <class Spec>
 struct Cascade {
@@ -87,6 +99,17 @@ struct Cascade {
         if (Spec::lead_moved(st.lead, now)) rebase(st.acc, st.lead, now);
         st.lead = now;
         if (!Spec::is_null(x)) Spec::acc_plus(st.acc, term(x, now), x, payload);
+    }
+
+    // Fold elements j0 .. j0 + 3 in, in that order. A spec with no dependent level may give
+    // lead_plus4, the same lead as four lead_plus in fewer steps.
+    __device__ static void absorb4(State& st, const float (&x)[4], int32_t j0, const float* payload) {
+        if constexpr (has_plus4<Spec>::value) {
+            st.lead = Spec::lead_plus4(st.lead, x, j0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) absorb(st, x[e], j0 + e, payload ? payload + e * kPayload : nullptr);
+        }
     }
 
     // Merge two partial states: both running values are rebased onto the merged lead.
@@ -142,6 +165,28 @@ __device__ __forceinline__ S shfl_xor_state(const S& s, int mask) {
     __builtin_memcpy(&out, w, sizeof(S));
     return out;
 }
+
+// The same through a DPP move within each row of 16 lanes (CTRL: a quad permute or a
+// mirror), without the LDS permute.
+template <int CTRL, class S>
+__device__ __forceinline__ S dpp_state(const S& s) {
+    static_assert(sizeof(S) % 4 == 0, "states are made of 32-bit words");
+    constexpr int W = int(sizeof(S) / 4);
+    uint32_t w[W];
+    __builtin_memcpy(w, &s, sizeof(S));
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = uint32_t(__builtin_amdgcn_update_dpp(0, int(w[i]), CTRL, 0xF, 0xF, false));
+    S out;
+    __builtin_memcpy(&out, w, sizeof(S));
+    return out;
+}
+
+// Whether a spec's merge is exact and independent of grouping (so any pairing of lanes that
+// joins disjoint groups gives the same state): kOrderFree.
+template <class S, class = void>
+struct order_free : std::false_type {};
+template <class S>
+struct order_free<S, std::void_t<decltype(S::kOrderFree)>> : std::bool_constant<S::kOrderFree> {};
 
 // ---------------------------------------------------------------- the max-led exponential cascades
 // d1 = max x (ascending max, identity -inf), H(d1) = e^(-d1), G(x) = e^x: the safe softmax's
@@ -211,50 +256,39 @@ struct SoftmaxWeighted : MaxLed<false> {
 };
 
 // ---------------------------------------------------------------- top-k, then softmax over the k
-// d1 = the K best (score, index) pairs under (score descending, index ascending); the softmax
-// over them is a final H applied once at the end, so no running value depends on d1.
+// d1 = the K best (score, index) pairs under (score descending, index ascending), held as
+// the 64-bit rank keys of topk.hpp (a branch-free insert per element, a bitonic merge of two
+// lists); the softmax over them is a final H applied once at the end, so no running value
+// depends on d1.
 template <int K>
 struct TopK {
     struct Lead {
-        float s[K];
-        int32_t i[K];
+        uint64_t key[K];
+        __device__ float score(int r) const { return topk::key_score(key[r]); }
+        __device__ int32_t index(int r) const { return topk::key_index(key[r]); }
     };
     struct H {};
     struct Acc {};
     static constexpr int kPayload = 0;
-    __device__ static bool better(float s1, int32_t i1, float s2, int32_t i2) {
-        return s1 > s2 || (s1 == s2 && i1 < i2);
-    }
+    static constexpr bool kOrderFree = true;      // the K best of a set: exact, any grouping
     __device__ static Lead lead_identity() {
         Lead l;
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            l.s[r] = kNegInf;
-            l.i[r] = 0x7FFFFFFF;
-        }
+        topk::clear<K>(l.key);
         return l;
     }
-    __device__ static void insert(Lead& l, float s, int32_t i) {
-#pragma unroll
-        for (int r = 0; r < K; ++r) {
-            if (better(s, i, l.s[r], l.i[r])) {
-                const float s2 = l.s[r];
-                const int32_t i2 = l.i[r];
-                l.s[r] = s;
-                l.i[r] = i;
-                s = s2;
-                i = i2;
-            }
-        }
-    }
     __device__ static Lead lead_plus(Lead l, float x, int32_t j) {
-        insert(l, x, j);
+        topk::insert<K>(l.key, topk::make_key(x, j));
+        return l;
+    }
+    // Four consecutive elements j0 .. j0 + 3 at once (the same list as four lead_plus).
+    __device__ static Lead lead_plus4(Lead l, const float (&x)[4], int32_t j0) {
+        topk::insert4<K>(l.key, topk::make_key(x[0], j0), topk::make_key(x[1], j0 + 1), topk::make_key(x[2], j0 + 2),
+                         topk::make_key(x[3], j0 + 3));
         return l;
     }
     __device__ static Lead lead_merge(const Lead& a, const Lead& b) {
         Lead l = a;
-#pragma unroll
-        for (int r = 0; r < K; ++r) insert(l, b.s[r], b.i[r]);
+        topk::merge<K>(l.key, b.key);
         return l;
     }
     __device__ static bool lead_is_identity(const Lead&) { return false; }

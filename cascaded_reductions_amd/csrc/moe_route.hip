@@ -16,13 +16,13 @@
 //    layout needs no transpose in memory;
 //  * the waves' partial scores are added through LDS in a fixed order (deterministic),
 //    then sixteen lanes per token keep sorted top-k lists over a sixteenth of the experts,
-//    merged by four DPP steps (moe_topk.hpp), and the first lane applies the softmax.
+//    merged by four DPP steps (topk.hpp), and the first lane applies the softmax.
 // Every workgroup reads the whole W_gate (E * Hd * 2 bytes, 0.5 MiB at 4096 x 64) from its
 // XCD's L2 and X once; the per-CU rate of those L2 reads bounds the kernel (the two-launch
 // form in moe_route_split.hip reads a range of W per CU instead, and exchanges partials).
 #include "common.hpp"
 #include "launch.hpp"
-#include "moe_topk.hpp"
+#include "topk.hpp"
 
 namespace rf {
 namespace {
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(Ring<NEB>::NW * 64) void moe_gate_kernel(const uint
     const int tok = tid >> 4, q = tid & 15;
     const int64_t t_out = t0 + tok;
     uint64_t list[K];
-    moe::clear<K>(list);
+    topk::clear<K>(list);
 #pragma unroll
     for (int e = 0; e < NEB; ++e) {
         const int ex = 16 * e + q;
@@ -216,12 +216,12 @@ __global__ __launch_bounds__(Ring<NEB>::NW * 64) void moe_gate_kernel(const uint
 #pragma unroll
         for (int w = 1; w < NW; ++w) s += part[(w * TB + tok) * PS + ex];
         if (scores && t_out < T) scores[t_out * E + ex] = s;
-        moe::insert<K>(list, moe::make_key(s, ex));
+        topk::insert<K>(list, topk::make_key(s, ex));
     }
-    moe::merge_row16<K>(list);
+    topk::merge_row16<K>(list);
     // Every lane of the row now holds the K best; the first k (k <= K) are the output, and the
     // softmax runs over exactly those k scores.
-    if (t_out < T && q == 0) moe::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
+    if (t_out < T && q == 0) topk::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
 }
 
 template <int NEB>

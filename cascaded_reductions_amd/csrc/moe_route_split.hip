@@ -12,7 +12,7 @@
 //  * a second launch adds each token's range partials in range order -- a fixed order, so
 //    results are deterministic -- and runs the top-k and the softmax in registers: sixteen
 //    lanes per token each keep a sorted top-k list over a sixteenth of the experts, merged
-//    with four DPP steps (moe_topk.hpp).
+//    with four DPP steps (topk.hpp).
 // Each CU reads only its range of W (64 KiB at 4096 x 64) instead of all of it, at the cost
 // of the partial scores' round trip (4 MiB at 2048 tokens) and a second launch; the kernel
 // boundary orders the two phases (the explainer's multi-kernel level, section 3.3).
@@ -21,7 +21,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
-#include "moe_topk.hpp"
+#include "topk.hpp"
 
 namespace rf {
 namespace {
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
     const int64_t t_out = int64_t(blockIdx.x) * (RED_T / 16) + (tid >> 4);
     const bool valid = t_out < T;
     uint64_t list[K];
-    moe::clear<K>(list);
+    topk::clear<K>(list);
     if (valid) {
         // Sum the range partials in range order (deterministic), loading RB ranges' worth
         // of this lane's experts before adding, so the loads overlap.
@@ -213,14 +213,14 @@ __global__ __launch_bounds__(RED_T) void moe_reduce_kernel(const float* __restri
 #pragma unroll
         for (int e = 0; e < NEB; ++e) {
             if (scores) scores[t_out * E + q * NEB + e] = sum[e];
-            moe::insert<K>(list, moe::make_key(sum[e], q * NEB + e));
+            topk::insert<K>(list, topk::make_key(sum[e], q * NEB + e));
         }
     }
     // Merge the sixteen lanes' lists of a token (one DPP row; a row is wholly valid or not).
-    moe::merge_row16<K>(list);
+    topk::merge_row16<K>(list);
     // Every lane of the row now holds the K best; the first k (k <= K) are the output, and
     // the softmax runs over exactly those k scores.
-    if (valid && q == 0) moe::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
+    if (valid && q == 0) topk::write_softmax<K>(list, k, idx + t_out * k, wout + t_out * k);
 }
 
 template <int NEB>

@@ -23,7 +23,8 @@ using namespace cascade;
 // G lanes fold one row (G in {4, 8, 16, 32, 64}; 64 / G rows per wave): lane i of the group
 // absorbs elements 4i .. 4i+3 of every 4G-element stretch (eight, or four for a large
 // state, streaming 16-byte loads in flight when there is no payload), then the group's
-// states are merged by xor shuffles within the group, in a fixed order.
+// states are merged by xor shuffles within the group, in a fixed order (for a merge that is
+// exact in any grouping, by DPP moves where the group fits a row of 16 lanes).
 template <class Spec, int G>
 __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* __restrict__ xr,
                                                                   const float* __restrict__ pr, int64_t N, int li) {
@@ -33,8 +34,7 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
     typename C::State st = C::identity();
     auto absorb4 = [&](const float4& v, int64_t j0) {
         const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) C::absorb(st, xs[e], int32_t(j0 + e), P ? pr + (j0 + e) * P : nullptr);
+        C::absorb4(st, xs, int32_t(j0), P ? pr + j0 * P : nullptr);
     };
     const bool vec = (N & 3) == 0;            // 16-byte loads need aligned rows
     // Eight loads in flight when only x is read (nontemporal: the row is read once), four for
@@ -87,8 +87,19 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
     const int64_t full = vec ? N / STRIDE * STRIDE : 0;
     for (; j0 < full; j0 += STRIDE) absorb4(*reinterpret_cast<const float4*>(xr + j0), j0);
     for (int64_t j = full + li; j < N; j += G) C::absorb(st, xr[j], int32_t(j), P ? pr + j * P : nullptr);
+    if constexpr (order_free<Spec>::value) {
+        // Any pairing that joins disjoint groups gives the same state: DPP moves within the
+        // row (lane xor 1, xor 2, then the half-row and row mirrors), LDS permutes above 16.
+        if constexpr (G >= 2) st = C::combine(st, dpp_state<0xB1>(st));
+        if constexpr (G >= 4) st = C::combine(st, dpp_state<0x4E>(st));
+        if constexpr (G >= 8) st = C::combine(st, dpp_state<0x141>(st));
+        if constexpr (G >= 16) st = C::combine(st, dpp_state<0x140>(st));
+        if constexpr (G >= 32) st = C::combine(st, shfl_xor_state(st, 16));
+        if constexpr (G >= 64) st = C::combine(st, shfl_xor_state(st, 32));
+    } else {
 #pragma unroll
-    for (int mask = G / 2; mask >= 1; mask >>= 1) st = C::combine(st, shfl_xor_state(st, mask));
+        for (int mask = G / 2; mask >= 1; mask >>= 1) st = C::combine(st, shfl_xor_state(st, mask));
+    }
     return st;
 }
 
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
         float e[K], den = 0.f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            e[i] = i < k ? __expf(st.lead.s[i] - st.lead.s[0]) : 0.f;
+            e[i] = i < k ? __expf(st.lead.score(i) - st.lead.score(0)) : 0.f;
             den += e[i];
         }
         const float inv = 1.f / den;
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
         for (int i = 0; i < K; ++i)
             if (i < k) {
                 out[r * k + i] = e[i] * inv;
-                out_idx[r * k + i] = st.lead.i[i];
+                out_idx[r * k + i] = st.lead.index(i);
             }
     }
 }
@@ -193,9 +204,11 @@ hipError_t launch_g(int kind, const float* x, const float* payload, int64_t R, i
 
 hipError_t launch_row_cascade(int kind, const float* x, const float* payload, int64_t R, int64_t N, int P, int k,
                               float* out, int32_t* out_idx, hipStream_t stream) {
-    // Lanes per row: enough that each lane absorbs at least 32 elements, at most a wave.
+    // Lanes per row: enough that each lane absorbs at least 32 elements (64 for top-k, where
+    // every merge level costs as much as folding in about five elements), at most a wave.
+    const int64_t per_lane = kind == 2 ? 64 : 32;
     int64_t g = 4;
-    while (g < 64 && N >= 32 * 2 * g) g *= 2;
+    while (g < 64 && N >= per_lane * 2 * g) g *= 2;
     switch (g) {
         case 4: return launch_g<4>(kind, x, payload, R, N, P, k, out, out_idx, stream);
         case 8: return launch_g<8>(kind, x, payload, R, N, P, k, out, out_idx, stream);
