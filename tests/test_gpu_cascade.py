@@ -36,7 +36,10 @@ def test_softmax_weighted(rf, R, N, P):
     assert_close(got, cascade.softmax_weighted(x, p), ATOL, RTOL, "o")
 
 
-@pytest.mark.parametrize("R,N", [(5, 8), (3, 255), (64, 1000), (2, 4099)])
+# Lanes per top-k row: 4 at N = 8, 255 and 256, 8 at 1000, 16 at 1500, 32 at 2048, 64 at 4099 and
+# 8192 (the four-at-a-time fold where N % 4 == 0, single inserts otherwise; DPP merges up to 16
+# lanes, LDS permutes above).
+@pytest.mark.parametrize("R,N", [(5, 8), (3, 255), (9, 256), (64, 1000), (5, 1500), (3, 2048), (2, 4099), (2, 8192)])
 @pytest.mark.parametrize("k", [1, 2, 5, 8])
 def test_topk_softmax(rf, R, N, k):
     # Scores on a grid of 1/4: many exact ties, which must resolve to the lower index.
@@ -46,6 +49,32 @@ def test_topk_softmax(rf, R, N, k):
     np.testing.assert_array_equal(host(idx), ri)
     assert_close(host(w), rw, ATOL, RTOL, "w")
 
+
+
+@pytest.mark.parametrize("R,N", [(4, 256), (3, 1000), (2, 4099)])
+def test_topk_softmax_nan_never_enters(rf, R, N):
+    """NaN scores rank nowhere: the result equals the oracle's on the row with each NaN
+    replaced by -inf (every row keeps far more than k finite scores)."""
+    x = _x(R, N, 35 + N)
+    g = np.random.default_rng(36 + N)
+    x[g.random((R, N)) < 0.1] = np.nan
+    x[0, :8] = np.nan                          # the first stretch of every lane of row 0
+    w, idx = rf.row_cascade("topk_softmax", dev_f32(x), k=8)
+    ri, rw = oracle.topk_softmax(np.where(np.isnan(x), -np.inf, x).astype(np.float64), 8)
+    np.testing.assert_array_equal(host(idx), ri)
+    assert_close(host(w), rw, ATOL, RTOL, "w")
+
+
+@pytest.mark.parametrize("N", [8, 256, 1000])
+def test_topk_softmax_signed_zero_ties(rf, N):
+    """+0 and -0 compare equal, so they tie and the lower index ranks first, whichever sign it
+    carries (the rank key turns -0 into +0)."""
+    x = np.full((2, N), -1.0, np.float32)
+    x[0, 3], x[0, 5] = 0.0, -0.0
+    x[1, 3], x[1, 5] = -0.0, 0.0
+    w, idx = rf.row_cascade("topk_softmax", dev_f32(x), k=2)
+    np.testing.assert_array_equal(host(idx), [[3, 5], [3, 5]])
+    np.testing.assert_array_equal(host(w), np.full((2, 2), 0.5))
 
 @pytest.mark.parametrize("R,N", SHAPES)
 def test_mean_var(rf, R, N):
