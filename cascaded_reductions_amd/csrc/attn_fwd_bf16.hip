@@ -82,7 +82,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
     constexpr int RPW = 64 / CH;              // key rows per wave load
     constexpr int NC = D / 16;                // K=16 slices of the head dimension
     constexpr int DB = D / 32;                // 32-wide output column blocks
-    static_assert(STAGES * STEP * 2 >= 2 * (DB * 16 + 2) * 64 * 4, "LDS must also hold the merge buffers");
+    static_assert(STAGES * STEP * 2 >= 2 * (DB * 16 + 2) * 64 * 4 + 2 * 32 * (D + 8) * 2,
+                  "LDS must also hold the merge buffers and the output staging tile");
 
     // A ring of STAGES K slots followed by a ring of STAGES V slots.
     __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STEP];
@@ -294,10 +295,14 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         // above it, probabilities again).
         const bool k_loader = ld_kind == 0;
         if (k_loader) {
+            // K tiles are issued only up to the half's last one, so no load is left in flight
+            // past the end of the loop; the waits below count what is actually in flight.
             issue(0, 0);
-            issue(1, 1);
-            issue(2, 2);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL) : "memory");   // K(0) is in
+            if (nsteps > 1) issue(1, 1);
+            if (nsteps > 2) issue(2, 2);
+            if (nsteps > 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL) : "memory");   // K(0) is in
+            else if (nsteps > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else {
             issue(0, 0);
         }
@@ -343,10 +348,15 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
             constexpr int KS1 = (J + 1) % 3;     // K(j + 1)
             constexpr int VP = (J + 2) % 3;      // V(j - 1)
             u32x4 kf[NC];
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");   // K(j + 1) / V(j - 1) are in
+            // K(j + 1) / V(j - 1) are in (a K loader with no K(j + 2) in flight waits for all).
+            if (k_loader && j + 2 >= nsteps) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
             __syncthreads();
-            if (k_loader) issue(j + 3, J);       // into K(j)'s slot
-            else issue(j + 1, KS1);              // into V(j - 2)'s slot
+            if (k_loader) {
+                if (j + 3 < nsteps) issue(j + 3, J);   // into K(j)'s slot
+            } else {
+                issue(j + 1, KS1);                  // into V(j - 2)'s slot
+            }
             load_k(KS1, kf);
             s_next = mfma_s(kf);
             if constexpr (!FIRST) pv(VP, pk_prev);
@@ -529,10 +539,15 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
         const float w1 = m_ref == kNegInf ? 0.f : exp2_fast(m_ref - M);
         const float w2 = m2 == kNegInf ? 0.f : exp2_fast(m2 - M);
         const float s = w1 * s_row + w2 * s2;
-        if (qrow < Sq) {
+        {
+            // The normalised rows go to an LDS staging tile (rows padded by 16 bytes), then out
+            // as whole 128-byte lines, 16 bytes per lane, with streaming stores: written through
+            // while the kernel runs, they leave no dirty lines for the end-of-kernel write-back,
+            // which otherwise holds the kernel's end (0.7 us at 8 x 12 x 512 x 512 x 64).
+            constexpr int SRW = D + 8;
+            uint16_t* stg = reinterpret_cast<uint16_t*>(mb + 2 * NR * 64) + qh * 32 * SRW;
             const float inv = 1.f / s;
             const float a1 = w1 * inv, a2 = w2 * inv;
-            uint16_t* dst = o + (bh * Sq + qrow) * D;
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -543,9 +558,19 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                     for (int e = 0; e < 4; ++e)
                         ov[e] = acc_o[b][4 * g4 + e] * a1 + src[(b * 16 + 4 * g4 + e) * 64 + lane] * a2;
                     const u32x2 w = {pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
-                    *reinterpret_cast<u32x2*>(dst + d) = w;
+                    *reinterpret_cast<u32x2*>(stg + l32 * SRW + d) = w;
                 }
-            if (lse && h == 0) lse[bh * Sq + qrow] = (M + __log2f(s)) * kLn2;
+            if (lse && h == 0 && qrow < Sq) lse[bh * Sq + qrow] = (M + __log2f(s)) * kLn2;
+            asm volatile("" ::: "memory");   // the wave reads back its own staging writes
+            constexpr int PPR = D / 8;               // 16-byte pieces per row
+#pragma unroll
+            for (int it = 0; it < 32 * PPR / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / PPR, piece = idx % PPR;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * SRW + piece * 8);
+                const int64_t grow = q0 + 32 * qh + row;
+                if (grow < Sq) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(o + (bh * Sq + grow) * D + piece * 8));
+            }
         }
     }
 }

@@ -37,6 +37,8 @@
 namespace rf {
 namespace {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // ------------------------------------------------------------------ 1. per-row quantisation
 
 constexpr int QT = 256;   // threads per workgroup
@@ -137,7 +139,12 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
     const float r = 1.0f / sigma;              // IEEE fp32 division (inf for a zero row; unused then)
     if (lane == 0) xs[row] = sigma;
 
-    auto quant8 = [&](const u32x4& t, int ch) { cr[ch] = codes8(t, sigma, r); };
+    // Streaming stores (each wave instruction writes 512 contiguous bytes): no dirty lines are
+    // left for the end-of-kernel write-back.
+    auto quant8 = [&](const u32x4& t, int ch) {
+        const uint2 c = codes8(t, sigma, r);
+        __builtin_nontemporal_store(u32x2{c.x, c.y}, reinterpret_cast<u32x2*>(cr + ch));
+    };
     if constexpr (NCT > 0) {
 #pragma unroll
         for (int i = 0; i < NCT; ++i) {
@@ -270,7 +277,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint8_t* s
             }
     }
     __syncthreads();
-    // 64 rows x 16 chunks of 16 bytes: each instruction writes 4 whole rows.
+    // 64 rows x 16 chunks of 16 bytes: each instruction writes 4 whole rows, with streaming
+    // stores, so no dirty lines are left for the end-of-kernel write-back.
     const int64_t nbase = n0 + wn * 128;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -282,7 +290,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint8_t* s
         if (m < M) {
             uint16_t* dst = y + m * N + n;
             if (n + 7 < N && ((N & 7) == 0)) {
-                *reinterpret_cast<u32x4*>(dst) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
             } else {
                 const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
 #pragma unroll

@@ -145,7 +145,10 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     const int64_t r = row_of<G>(li);
     if (r >= R) return;
     const auto st = fold_row<TopK<K>, G>(x + r * N, nullptr, N, li);
-    if (li == 0) {
+    // Every lane of the row's group holds the merged list; lane li writes entries 2 li and
+    // 2 li + 1, so a wave's stores cover its rows' outputs contiguously, as whole lines (k even)
+    // with streaming stores that leave no dirty lines for the end-of-kernel write-back.
+    {
         float e[K], den = 0.f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
@@ -153,12 +156,30 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
             den += e[i];
         }
         const float inv = 1.f / den;
+        typedef float fx2 __attribute__((ext_vector_type(2)));
+        typedef int32_t ix2 __attribute__((ext_vector_type(2)));
+        const int i0 = 2 * li;
+        float w0 = 0.f, w1 = 0.f;
+        int32_t x0 = 0, x1 = 0;
 #pragma unroll
-        for (int i = 0; i < K; ++i)
-            if (i < k) {
-                out[r * k + i] = e[i] * inv;
-                out_idx[r * k + i] = st.lead.index(i);
+        for (int i = 0; i < K; ++i) {
+            if (i == i0) { w0 = e[i] * inv; x0 = st.lead.index(i); }
+            if (i == i0 + 1) { w1 = e[i] * inv; x1 = st.lead.index(i); }
+        }
+        if (i0 + 1 < k) {
+            if ((k & 1) == 0) {
+                const fx2 wv = {w0, w1};
+                const ix2 iv = {x0, x1};
+                __builtin_nontemporal_store(wv, reinterpret_cast<fx2*>(out + r * k + i0));
+                __builtin_nontemporal_store(iv, reinterpret_cast<ix2*>(out_idx + r * k + i0));
+            } else {
+                out[r * k + i0] = w0; out[r * k + i0 + 1] = w1;
+                out_idx[r * k + i0] = x0; out_idx[r * k + i0 + 1] = x1;
             }
+        } else if (i0 < k) {
+            out[r * k + i0] = w0;
+            out_idx[r * k + i0] = x0;
+        }
     }
 }
 
