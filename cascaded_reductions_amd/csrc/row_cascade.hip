@@ -51,8 +51,21 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
             const fx4 t = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(xr + j0 + u * STRIDE));
             v[u] = make_float4(t[0], t[1], t[2], t[3]);
         }
+        if constexpr (has_plus4<Spec>::value || P != 0) {   // (this loop runs only without a payload)
 #pragma unroll
-        for (int u = 0; u < UN; ++u) absorb4(v[u], j0 + u * STRIDE);
+            for (int u = 0; u < UN; ++u) absorb4(v[u], j0 + u * STRIDE);
+        } else {
+            // The whole batch at once: one correction for 4 UN elements.
+            float xs[4 * UN];
+            int32_t js[4 * UN];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                xs[4 * u] = v[u].x; xs[4 * u + 1] = v[u].y; xs[4 * u + 2] = v[u].z; xs[4 * u + 3] = v[u].w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) js[4 * u + e] = int32_t(j0 + u * STRIDE + e);
+            }
+            C::template absorb_n<4 * UN>(st, xs, js);
+        }
     }
     // With a payload of P <= 4 values, UPW stretches of x and payload (1 + P 16-byte loads
     // each) are loaded before any is absorbed, so 8-10 loads are in flight per lane; the
@@ -78,10 +91,10 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
                 }
             }
 #pragma unroll
-            for (int u = 0; u < UPW; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    C::absorb(st, xv[u][e], int32_t(j0 + u * STRIDE + e), &pv[u][e * P]);
+            for (int u = 0; u < UPW; ++u) {
+                const float xs[4] = {xv[u][0], xv[u][1], xv[u][2], xv[u][3]};
+                C::absorb4(st, xs, int32_t(j0 + u * STRIDE), pv[u]);
+            }
         }
     }
     const int64_t full = vec ? N / STRIDE * STRIDE : 0;
