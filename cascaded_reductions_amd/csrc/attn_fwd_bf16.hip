@@ -38,6 +38,8 @@
 //  * Workgroups of one head are placed on one XCD (workgroups are dispatched
 //    round-robin over the 8 XCDs), so the head's K and V are fetched into that
 //    XCD's L2 once.
+//  * The output leaves through an LDS staging tile as whole 128-byte lines with
+//    streaming stores, so no dirty lines wait in L2 for the end-of-kernel write-back.
 #include <type_traits>
 
 #include "attn_tiles.hpp"

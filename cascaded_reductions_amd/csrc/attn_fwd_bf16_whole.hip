@@ -48,7 +48,10 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     constexpr int WL = TILE * 2 / 1024;      // wave loads per tile
     constexpr int NC = D / 16;               // K=16 slices of the head dimension
     constexpr int DB = D / 32;               // 32-wide output column blocks
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NT * TILE];   // K tiles, then V tiles
+    // K tiles, then V tiles; the output staging tiles reuse the region at the end.
+    constexpr int SRW = D + 8;                // staging row stride (bf16): 16 bytes of padding
+    constexpr int LDS_ELEMS = 2 * NT * TILE > 4 * 32 * SRW ? 2 * NT * TILE : 4 * 32 * SRW;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
     uint16_t* const ks = smem;
     uint16_t* const vs = smem + NT * TILE;
 
@@ -169,11 +172,15 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         }
     }
 
-    // Epilogue: o = o~ / s (the two lane halves hold the two halves of each tile's keys).
+    // Epilogue: o = o~ / s (the two lane halves hold the two halves of each tile's keys). The
+    // wave's 32 rows go to an LDS staging tile (in the K/V region, free once every wave is
+    // past its PV), then out as whole lines, 16 bytes per lane, with
+    // streaming stores that leave no dirty lines for the end-of-kernel write-back.
     const float srow = ssum + __shfl_xor(ssum, 32, 64);
-    if (qrow < Sq) {
+    __syncthreads();
+    uint16_t* stg = smem + wave * 32 * SRW;
+    {
         const float inv = 1.f / srow;
-        uint16_t* dst = o + (bh * Sq + qrow) * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -181,9 +188,19 @@ void attn_whole_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 const int d = 32 * b + g4 * 8 + 4 * h;
                 const u32x2 w = {pack2(acc_o[b][4 * g4] * inv, acc_o[b][4 * g4 + 1] * inv),
                                  pack2(acc_o[b][4 * g4 + 2] * inv, acc_o[b][4 * g4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(dst + d) = w;
+                *reinterpret_cast<u32x2*>(stg + l32 * SRW + d) = w;
             }
-        if (lse && h == 0) lse[bh * Sq + qrow] = (m2 + __log2f(srow)) * kLn2;
+        if (lse && h == 0 && qrow < Sq) lse[bh * Sq + qrow] = (m2 + __log2f(srow)) * kLn2;
+    }
+    asm volatile("" ::: "memory");            // the wave reads back its own staging writes
+    constexpr int PPR = D / 8;                // 16-byte pieces per row
+#pragma unroll
+    for (int it = 0; it < 32 * PPR / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int row = idx / PPR, piece = idx % PPR;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * SRW + piece * 8);
+        const int64_t grow = q0 + 32 * wave + row;
+        if (grow < Sq) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(o + (bh * Sq + grow) * D + piece * 8));
     }
 }
 

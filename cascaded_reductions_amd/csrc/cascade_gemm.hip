@@ -18,6 +18,7 @@
 // kernels form O^T = V^T P^T): W^T comes from LDS through the transposing read
 // (ds_read_b64_tr_b16) and P^T is the packed weights as each lane computes them, so every
 // lane owns one row and the lead's correction is a per-lane scale.
+// The output rows leave through an LDS staging tile as whole lines with streaming stores.
 #include <type_traits>
 
 #include "attn_tiles.hpp"
