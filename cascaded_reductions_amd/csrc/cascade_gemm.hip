@@ -12,9 +12,10 @@
 // runs on v_mfma_f32_32x32x16_bf16 with each weight split into two bf16 parts.
 //
 // gfx950 mapping: a workgroup of 4 waves owns 128 rows (32 per wave) and walks K in chunks
-// of 32. Each chunk's W slice [32 x N] bf16 and each wave's X slice [32 x 32] fp32 go to LDS
-// by direct global-to-LDS loads issued two chunks ahead (3-slot rings), so no registers
-// hold data in flight. The output is formed as Y^T = W^T P^T (as the attention
+// of 32, starting at a chunk that differs between workgroups (the cascade's result does not
+// depend on the order in which a row's entries are absorbed). Each chunk's W slice [32 x N]
+// bf16 and each wave's X slice [32 x 32] fp32 go to LDS by direct global-to-LDS loads issued
+// two chunks ahead (3-slot rings), so no registers hold data in flight. The output is formed as Y^T = W^T P^T (as the attention
 // kernels form O^T = V^T P^T): W^T comes from LDS through the transposing read
 // (ds_read_b64_tr_b16) and P^T is the packed weights as each lane computes them, so every
 // lane owns one row and the lead's correction is a per-lane scale.
@@ -118,9 +119,18 @@ __global__ __launch_bounds__(NW * 64, 2) void cascade_gemm_kernel(const float* _
         const int lc = pc ^ attn_v_swz<N>(r);
         w_off[l] = uint32_t(r * N + lc * 8);  // element offset within the slice
     }
+    // Workgroups start their walk over K at different chunks and wrap around. Rows are K * 4
+    // bytes apart, so when every workgroup reads the same columns at once the chip's reads
+    // pile onto a few memory channels; the start is spread over the chunks per XCD
+    // (workgroup b runs on XCD b % 8, so b >> 3 numbers an XCD's workgroups).
+    const int first = int((blockIdx.x >> 3) % unsigned(nchunks));
+    auto chunk_of = [&](int t) {               // the chunk walked at step t (t >= nchunks: the last)
+        const int c = first + (t < nchunks ? t : nchunks - 1);
+        return c < nchunks ? c : c - nchunks;
+    };
     auto issue = [&](int t) {
         const int st = t % STAGES;
-        const int k0 = (t < nchunks ? t : nchunks - 1) * KC;
+        const int k0 = chunk_of(t) * KC;
         const uint32_t xl = xl_base + uint32_t(st * XSLOT);
         const unsigned char* wl = reinterpret_cast<const unsigned char*>(wring) + st * WSLOT + wave * WPW * 1024;
         if (k0 + KC <= K32) {                 // the whole chunk lies inside K (wave-uniform)
@@ -185,12 +195,13 @@ __global__ __launch_bounds__(NW * 64, 2) void cascade_gemm_kernel(const float* _
 #pragma unroll
             for (int e = 0; e < 4; ++e) xv[4 * c + e] = v[e] * xscale;
         }
-        if ((t + 1) * KC > K32) {             // the last chunk runs past K (wave-uniform): null entries
+        const int kc0 = chunk_of(t) * KC;
+        if (kc0 + KC > K32) {                 // the last chunk runs past K (wave-uniform): null entries
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (t * KC + 8 * c + 4 * h + e >= K32) xv[4 * c + e] = SOFTMAX ? kNegInf : 0.f;
+                    if (kc0 + 8 * c + 4 * h + e >= K32) xv[4 * c + e] = SOFTMAX ? kNegInf : 0.f;
         }
         // The lead over this chunk: the lane's 16 values, then its partner lane (l ^ 32).
         Lead tl = lead;

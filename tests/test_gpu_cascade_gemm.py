@@ -115,3 +115,41 @@ def test_deterministic(rf):
     b = rf.cascade_gemm("softmax", dev_f32(x), dev_bf16(wb))
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kind", ["softmax", "absmax"])
+@pytest.mark.parametrize("M,K,N", [(8200, 1000, 64), (4200, 100, 128)])
+def test_many_workgroups_ragged_k(rf, kind, M, K, N):
+    """Enough workgroups (of 128 rows) that they start their walk over K at different chunks,
+    with a ragged last chunk that, at K = 100 (4 chunks), some workgroups meet first."""
+    x, wb = _inputs(M, K, N, 400 + M + K, scale=3.0 if kind == "softmax" else 1.0)
+    x[5, :] = -np.inf if kind == "softmax" else 0.0
+    x[5, K - 1] = 2.0                                  # the only entry sits in the ragged chunk
+    y, stat = _run(rf, kind, x, wb)
+    ref = cascade.softmax_gemm if kind == "softmax" else cascade.absmax_gemm
+    ry, rs = ref(x, bf16_bits_to_f32(wb))
+    assert_close(y, ry, ATOL, RTOL, "y")
+    _tight(y, ry, x, wb, kind)
+    if kind == "softmax":
+        assert_close(stat, rs, ATOL, RTOL, "lse")
+        np.testing.assert_array_equal(y[5], bf16_bits_to_f32(wb)[K - 1].astype(np.float64))
+    else:
+        np.testing.assert_array_equal(stat.astype(np.float32), rs.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["softmax", "absmax"])
+def test_full_size_sampled(rf, kind):
+    """The benchmarked shape, 65536 x 1024 fp32 against 1024 x 128 bf16, in the benchmarked
+    launch; every 61st row (and the last) against the oracle."""
+    M, K, N = 65536, 1024, 128
+    x, wb = _inputs(M, K, N, 500, scale=3.0 if kind == "softmax" else 1.0)
+    y, stat = _run(rf, kind, x, wb)
+    rows = np.r_[np.arange(0, M, 61), M - 1]
+    ref = cascade.softmax_gemm if kind == "softmax" else cascade.absmax_gemm
+    ry, rs = ref(x[rows], bf16_bits_to_f32(wb))
+    assert_close(y[rows], ry, ATOL, RTOL, "y")
+    _tight(y[rows], ry, x[rows], wb, kind)
+    if kind == "softmax":
+        assert_close(stat[rows], rs, ATOL, RTOL, "lse")
+    else:
+        np.testing.assert_array_equal(stat[rows].astype(np.float32), rs.astype(np.float32))
