@@ -1,6 +1,6 @@
 """GPU parity: rf_row_cascade (the generic incremental template's instances) against the
 plain multi-pass definitions in oracle/cascade.py. fp32 inputs and fp32 accumulation:
-|g - r| <= 1e-5 + 1e-5 |r|; top-k indices bit-exact."""
+|g - r| <= 1e-5; top-k indices bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,7 @@ from tests.gpu_util import assert_close, dev_f32, host
 
 pytestmark = pytest.mark.gpu
 
-ATOL = RTOL = 1e-5
+ATOL, RTOL = 1e-5, 0.0       # fp32 inputs: 1e-5 absolute
 SHAPES = [(1, 1), (5, 3), (3, 255), (4, 256), (2, 257), (64, 1000), (7, 4096), (2, 4099)]
 
 
