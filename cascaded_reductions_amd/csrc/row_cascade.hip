@@ -2,8 +2,9 @@
 //
 // A group of G lanes folds one row of x [R, N] (fp32; G from 4 to 64 so that every lane
 // absorbs at least 32 elements): lane i absorbs elements 4i .. 4i+3 of every 4G-element
-// stretch (16-byte loads), then the group's states are merged by xor shuffles in a fixed
-// order and the group's first lane writes the row's result. The instances are the cascades
+// stretch (16-byte loads; i, i+G, i+2G, i+3G with a 4-value payload), then the group's
+// states are merged by xor shuffles in a fixed order and the group's first lane writes the
+// row's result. The instances are the cascades
 // the technical summary "RedFuser: An Automatic Operator Fusion Framework for Cascaded
 // Reductions on AI Accelerators" (Methodologie 1-2) and the explainer
 // "RedFuser框架：AI加速器中的算子融合技术解析" (sections 2.2, 4.1, 4.2) use as examples,
@@ -21,10 +22,11 @@ namespace {
 using namespace cascade;
 
 // G lanes fold one row (G in {4, 8, 16, 32, 64}; 64 / G rows per wave): lane i of the group
-// absorbs elements 4i .. 4i+3 of every 4G-element stretch (eight, or four for a large
-// state, streaming 16-byte loads in flight when there is no payload), then the group's
-// states are merged by xor shuffles within the group, in a fixed order (for a merge that is
-// exact in any grouping, by DPP moves where the group fits a row of 16 lanes).
+// absorbs elements 4i .. 4i+3 of every 4G-element stretch, or i + G e (e = 0..3) with a
+// 4-value payload (eight, or four for a large state, streaming 16-byte loads in flight when
+// there is no payload), then the group's states are merged by xor shuffles within the group,
+// in a fixed order (for a merge that is exact in any grouping, by DPP moves where the group
+// fits a row of 16 lanes).
 template <class Spec, int G>
 __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* __restrict__ xr,
                                                                   const float* __restrict__ pr, int64_t N, int li) {
@@ -67,10 +69,15 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
             C::template absorb_n<4 * UN>(st, xs, js);
         }
     }
-    // With a payload of P <= 4 values, UPW stretches of x and payload (1 + P 16-byte loads
-    // each) are loaded before any is absorbed, so 8-10 loads are in flight per lane; the
-    // elements are absorbed in the same order as one stretch at a time.
-    constexpr int UPW = P == 0 ? 1 : P <= 1 ? 4 : P <= 2 ? 3 : P <= 4 ? 2 : 1;
+    // With a payload of P <= 4 values, UPW stretches of x and payload are loaded before any
+    // is absorbed. For P = 1 and 2 a lane takes the 4 consecutive elements 4i .. 4i+3 of a
+    // stretch (1 + P 16-byte loads). For P = 4 an element's payload is a whole 16-byte piece,
+    // so lane i takes elements i, i + G, i + 2G and i + 3G instead: each of its x and payload
+    // loads then reads, across the group, one contiguous run (G x 4 and G x 16 bytes), where
+    // the consecutive mapping's payload loads touch twice the lines per instruction with a
+    // 64-byte lane stride (measured 98.5 against 111.7 us at 4096 x 8192). The cascade's
+    // result does not depend on the order in which a lane absorbs its elements.
+    constexpr int UPW = P == 0 ? 1 : P <= 1 ? 4 : P <= 2 ? 3 : P <= 4 ? 4 : 1;
     if constexpr (UPW > 1) {
         typedef float fx4 __attribute__((ext_vector_type(4)));
         const int64_t fullp = vec ? N / (UPW * STRIDE) * (UPW * STRIDE) : 0;
@@ -79,15 +86,27 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
             float pv[UPW][4 * P];
 #pragma unroll
             for (int u = 0; u < UPW; ++u) {
-                const int64_t j = j0 + u * STRIDE;
-                xv[u] = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(xr + j));
+                if constexpr (P == 4) {
+                    const int64_t je0 = j0 - 4 * li + u * STRIDE + li;   // the lane's first element
 #pragma unroll
-                for (int c = 0; c < P; ++c) {
-                    // Cached loads: lane i's P 16-byte loads of a stretch share cache lines
-                    // with lane i + 1's, so a streaming hint would fetch each line again.
-                    const fx4 t = *reinterpret_cast<const fx4*>(pr + j * P + 4 * c);
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t je = je0 + int64_t(G) * e;
+                        xv[u][e] = __builtin_nontemporal_load(xr + je);
+                        const fx4 t = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(pr + je * 4));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pv[u][4 * c + e] = t[e];
+                        for (int c = 0; c < 4; ++c) pv[u][4 * e + c] = t[c];
+                    }
+                } else {
+                    const int64_t j = j0 + u * STRIDE;
+                    xv[u] = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(xr + j));
+#pragma unroll
+                    for (int c = 0; c < P; ++c) {
+                        // Cached loads: lane i's P 16-byte loads of a stretch share cache lines
+                        // with lane i + 1's, so a streaming hint would fetch each line again.
+                        const fx4 t = *reinterpret_cast<const fx4*>(pr + j * P + 4 * c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[u][4 * c + e] = t[e];
+                    }
                 }
             }
 #pragma unroll
