@@ -15,10 +15,10 @@
 // of 32, starting at a chunk that differs between workgroups (the cascade's result does not
 // depend on the order in which a row's entries are absorbed). Each chunk's W slice [32 x N]
 // bf16 and each wave's X slice [32 x 32] fp32 go to LDS by direct global-to-LDS loads issued
-// two chunks ahead (3-slot rings), so no registers hold data in flight. The output is formed as Y^T = W^T P^T (as the attention
-// kernels form O^T = V^T P^T): W^T comes from LDS through the transposing read
-// (ds_read_b64_tr_b16) and P^T is the packed weights as each lane computes them, so every
-// lane owns one row and the lead's correction is a per-lane scale.
+// two chunks ahead (3-slot rings), so no registers hold data in flight. The output is formed
+// as Y^T = W^T P^T (as the attention kernels form O^T = V^T P^T): W^T comes from LDS through
+// the transposing read (ds_read_b64_tr_b16) and P^T is the packed weights as each lane
+// computes them, so every lane owns one row and the lead's correction is a per-lane scale.
 // The output rows leave through an LDS staging tile as whole lines with streaming stores.
 #include <type_traits>
 

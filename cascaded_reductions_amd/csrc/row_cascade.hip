@@ -4,9 +4,9 @@
 // absorbs at least 32 elements): lane i absorbs elements 4i .. 4i+3 of every 4G-element
 // stretch (16-byte loads; i, i+G, i+2G, i+3G with a 4-value payload), then the group's
 // states are merged by xor shuffles in a fixed order and the group's first lane writes the
-// row's result. The instances are the cascades
-// the technical summary "RedFuser: An Automatic Operator Fusion Framework for Cascaded
-// Reductions on AI Accelerators" (Methodologie 1-2) and the explainer
+// row's result. The instances are the cascades the technical summary "RedFuser: An
+// Automatic Operator Fusion Framework for Cascaded Reductions on AI Accelerators"
+// (Methodologie 1-2) and the explainer
 // "RedFuser框架：AI加速器中的算子融合技术解析" (sections 2.2, 4.1, 4.2) use as examples,
 // plus mean/variance as a cascade outside attention:
 //   logsumexp                 out[r] = max + ln(sum exp(x - max))
