@@ -121,3 +121,37 @@ def test_softmax_weighted_masked(rf, R, N, P):
     assert_close(got, cascade.softmax_weighted(x, p), ATOL, RTOL, "o")
     # the row masked except for its last element returns that element's payload
     np.testing.assert_array_equal(got[0], p[0, -1].astype(np.float64))
+
+
+# The benchmarked workloads at full size, in the benchmarked launch: inputs drawn on the device
+# from a seeded generator, every output computed, every 61st row (and the last) checked against
+# the oracle on the host.
+FULL = [("logsumexp", 16384, 16384, 0, 0), ("mean_var", 16384, 16384, 0, 0),
+        ("softmax_weighted", 4096, 8192, 4, 0), ("topk_softmax", 262144, 256, 0, 8)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kind,R,N,P,k", FULL)
+def test_workload_full_size_sampled(rf, kind, R, N, P, k):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(80 + R % 97)
+    x = torch.randn(R, N, device="cuda", generator=g)
+    pay = torch.randn(R, N, P, device="cuda", generator=g) if P else None
+    got = rf.row_cascade(kind, x, pay, k=k)
+    torch.cuda.synchronize()
+    rows = torch.cat([torch.arange(0, R, 61), torch.tensor([R - 1])]).to("cuda")
+    xs = host(x.index_select(0, rows)).astype(np.float32)
+    if kind == "topk_softmax":
+        w, idx = got
+        ridx, rw = cascade.topk_softmax(xs.astype(np.float64), k)
+        np.testing.assert_array_equal(host(idx.index_select(0, rows)), ridx)
+        assert_close(host(w.index_select(0, rows)), rw, ATOL, RTOL, "w")
+        return
+    g_rows = host(got.index_select(0, rows))
+    if kind == "logsumexp":
+        ref = cascade.logsumexp(xs)
+    elif kind == "mean_var":
+        ref = cascade.mean_var(xs)
+    else:
+        ref = cascade.softmax_weighted(xs, host(pay.index_select(0, rows)).astype(np.float32))
+    assert_close(g_rows, ref, ATOL, RTOL, kind)
