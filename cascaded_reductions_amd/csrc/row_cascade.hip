@@ -69,16 +69,19 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
             C::template absorb_n<4 * UN>(st, xs, js);
         }
     }
-    // With a payload of P <= 4 values, UPW stretches of x and payload are loaded before any
+    // With a payload of P <= 8 values, UPW stretches of x and payload are loaded before any
     // is absorbed. For P = 1 and 2 a lane takes the 4 consecutive elements 4i .. 4i+3 of a
-    // stretch (1 + P 16-byte loads). For P = 4 an element's payload is a whole 16-byte piece,
-    // so lane i takes elements i, i + G, i + 2G and i + 3G instead: each of its x and payload
-    // loads then reads, across the group, one contiguous run (G x 4 and G x 16 bytes), where
-    // the consecutive mapping's payload loads touch twice the lines per instruction with a
-    // 64-byte lane stride (measured 98.5 against 111.7 us at 4096 x 8192). The cascade's
-    // result does not depend on the order in which a lane absorbs its elements.
-    constexpr int UPW = P == 0 ? 1 : P <= 1 ? 4 : P <= 2 ? 3 : P <= 4 ? 4 : 1;
-    if constexpr (UPW > 1) {
+    // stretch (1 + P 16-byte loads). For P = 4 and 8 an element's payload is one or two whole
+    // 16-byte pieces, so lane i takes elements i, i + G, i + 2G and i + 3G instead ("spread"):
+    // its x loads then read, across the group, one contiguous run of G x 4 bytes and its
+    // payload loads runs of 16 bytes at a P x 4-byte stride, where the consecutive mapping's
+    // payload loads have a 4 P x 4-byte lane stride (measured at 4096 x 8192: P = 4 98.5
+    // against 111.7 us, P = 8 186 against 313 us; P = 16 was slower spread, 551 against 464 us,
+    // and keeps the consecutive mapping). The cascade's result does not depend on the order in
+    // which a lane absorbs its elements.
+    constexpr bool SPREAD = P == 4 || P == 8;
+    constexpr int UPW = P == 0 ? 1 : P <= 1 ? 4 : P <= 2 ? 3 : P <= 4 ? 4 : P <= 8 ? 2 : 1;
+    if constexpr (UPW > 1 || SPREAD) {
         typedef float fx4 __attribute__((ext_vector_type(4)));
         const int64_t fullp = vec ? N / (UPW * STRIDE) * (UPW * STRIDE) : 0;
         for (; j0 < fullp; j0 += UPW * STRIDE) {
@@ -86,15 +89,18 @@ __device__ __forceinline__ typename Cascade<Spec>::State fold_row(const float* _
             float pv[UPW][4 * P];
 #pragma unroll
             for (int u = 0; u < UPW; ++u) {
-                if constexpr (P == 4) {
+                if constexpr (SPREAD) {
                     const int64_t je0 = j0 - 4 * li + u * STRIDE + li;   // the lane's first element
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int64_t je = je0 + int64_t(G) * e;
                         xv[u][e] = __builtin_nontemporal_load(xr + je);
-                        const fx4 t = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(pr + je * 4));
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) pv[u][4 * e + c] = t[c];
+                        for (int c = 0; c < P / 4; ++c) {
+                            const fx4 t = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(pr + je * P + 4 * c));
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) pv[u][P * e + 4 * c + i] = t[i];
+                        }
                     }
                 } else {
                     const int64_t j = j0 + u * STRIDE;
