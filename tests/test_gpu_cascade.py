@@ -155,3 +155,26 @@ def test_workload_full_size_sampled(rf, kind, R, N, P, k):
     else:
         ref = cascade.softmax_weighted(xs, host(pay.index_select(0, rows)).astype(np.float32))
     assert_close(g_rows, ref, ATOL, RTOL, kind)
+
+
+# Seeded random shapes: row counts and widths drawn across the lane-group sizes (4 to 64),
+# the aligned and unaligned paths, and the spread payload mapping's stretch counts.
+_RNG_SHAPES = np.random.default_rng(2024)
+RANDOM = [(int(_RNG_SHAPES.integers(1, 300)), int(_RNG_SHAPES.integers(1, 9000))) for _ in range(12)]
+
+
+@pytest.mark.parametrize("R,N", RANDOM)
+def test_random_shapes(rf, R, N):
+    g = np.random.default_rng(R * 10007 + N)
+    x = (g.standard_normal((R, N)) * 3).astype(np.float32)
+    assert_close(host(rf.row_cascade("logsumexp", dev_f32(x))), cascade.logsumexp(x), ATOL, RTOL, "lse")
+    assert_close(host(rf.row_cascade("mean_var", dev_f32(x))), cascade.mean_var(x), ATOL, RTOL, "mean/var")
+    for P in (4, 8):
+        p = g.standard_normal((R, N, P)).astype(np.float32)
+        got = host(rf.row_cascade("softmax_weighted", dev_f32(x), dev_f32(p)))
+        assert_close(got, cascade.softmax_weighted(x, p), ATOL, RTOL, f"o (P = {P})")
+    k = int(min(8, N))
+    w, idx = rf.row_cascade("topk_softmax", dev_f32(x), k=k)
+    ri, rw = oracle.topk_softmax(x.astype(np.float64), k)
+    np.testing.assert_array_equal(host(idx), ri)
+    assert_close(host(w), rw, ATOL, RTOL, "w")

@@ -153,3 +153,24 @@ def test_full_size_sampled(rf, kind):
         assert_close(stat[rows], rs, ATOL, RTOL, "lse")
     else:
         np.testing.assert_array_equal(stat[rows].astype(np.float32), rs.astype(np.float32))
+
+
+_RNG_SHAPES = np.random.default_rng(4048)
+RANDOM = [(int(_RNG_SHAPES.integers(1, 6000)), 4 * int(_RNG_SHAPES.integers(1, 700)),
+           int(_RNG_SHAPES.choice([64, 128]))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("M,K,N", RANDOM)
+def test_random_shapes(rf, M, K, N):
+    """Seeded random shapes (up to 47 workgroups, so their walks over K start at different
+    chunks, and K with or without a ragged last chunk), both kinds."""
+    for kind, ref_fn, scale in (("softmax", cascade.softmax_gemm, 3.0), ("absmax", cascade.absmax_gemm, 1.0)):
+        x, wb = _inputs(M, K, N, 600 + M + K + N, scale=scale)
+        y, stat = _run(rf, kind, x, wb)
+        ry, rs = ref_fn(x, bf16_bits_to_f32(wb))
+        assert_close(y, ry, ATOL, RTOL, f"y ({kind})")
+        _tight(y, ry, x, wb, kind)
+        if kind == "softmax":
+            assert_close(stat, rs, ATOL, RTOL, "lse")
+        else:
+            np.testing.assert_array_equal(stat.astype(np.float32), rs.astype(np.float32))
