@@ -199,3 +199,18 @@ def test_bf16_modes_agree_below_threshold(rf):
     a, _ = _run_mode(rf, inp, "auto")
     w, _ = _run_mode(rf, inp, "whole_row")
     assert np.array_equal(a, w)
+
+
+# Seeded random shapes through the automatic mode (incremental or whole-row by key length).
+_RNG_SHAPES = np.random.default_rng(512)
+RANDOM_BF16 = [(int(_RNG_SHAPES.integers(1, 3)), int(_RNG_SHAPES.integers(1, 5)), int(_RNG_SHAPES.integers(1, 700)),
+                int(_RNG_SHAPES.integers(1, 1200)), int(_RNG_SHAPES.choice([64, 128]))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D", RANDOM_BF16)
+def test_bf16_random_shapes(rf, B, H, Sq, Sk, D):
+    inp = attn_inputs(B, H, Sq, Sk, D, "bf16", seed=900 + Sq + Sk + D, scale=float(1.0 / np.sqrt(D)))
+    o, lse = _run(rf, inp)
+    ro, rl = _ref(inp)
+    assert_close(o, ro, BF16_ATOL, BF16_RTOL, "O")
+    assert_close(lse, rl, BF16_ATOL, BF16_RTOL, "lse")
