@@ -164,3 +164,14 @@ def test_one_call_decode(rf, B, H, L, D, nseg, out_dtype):
     atol, rtol = (ATOL, RTOL) if out_dtype == torch.bfloat16 else (1e-3, 1e-3)
     assert_close(host(o), ro, atol, rtol, "O")
     assert_close(host(lse), rl, ATOL, RTOL, "lse")
+
+
+_RNG_SHAPES = np.random.default_rng(1024)
+RANDOM = [(int(_RNG_SHAPES.integers(1, 4)), int(_RNG_SHAPES.integers(1, 9)), int(_RNG_SHAPES.integers(1, 3000)),
+           int(_RNG_SHAPES.choice([64, 128])), int(_RNG_SHAPES.integers(1, 40))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("B,H,L,D,nseg", RANDOM)
+def test_random_shapes(rf, B, H, L, D, nseg):
+    """Seeded random shapes and segment counts (including more segments than keys)."""
+    _check_case(rf, B, H, L, D, nseg, seed=1300 + L + nseg)

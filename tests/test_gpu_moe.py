@@ -94,3 +94,17 @@ def test_forms_agree(rf):
     b = _check(rf, x, w, 2, check_scores=False, split=True)
     assert np.array_equal(a[0], b[0])
     assert_close(b[1], a[1], 1e-5, 1e-5, "weights of the two forms")
+
+
+_RNG_SHAPES = np.random.default_rng(77)
+RANDOM = [(int(_RNG_SHAPES.integers(1, 600)), 32 * int(_RNG_SHAPES.integers(1, 160)),
+           16 * int(_RNG_SHAPES.integers(1, 17)), int(_RNG_SHAPES.integers(1, 9))) for _ in range(8)]
+
+
+@pytest.mark.parametrize("T,Hd,E,k", RANDOM)
+@pytest.mark.parametrize("split", [False, True], ids=["one_launch", "split"])
+def test_random_shapes(rf, T, Hd, E, k, split):
+    """Seeded random token counts, hidden sizes, expert counts and k (indices bit-exact)."""
+    k = min(k, E)
+    x, w = moe_inputs(T, Hd, E, k, seed=1900 + T + E + k, w_std=0.5 if Hd < 1024 else 0.02)
+    _check(rf, x, w, k, split=split)

@@ -220,3 +220,16 @@ def test_signed_zero_inputs(rf, form):
     wq = np.zeros((8, 128), np.uint8)
     np.fill_diagonal(wq, 0x38)
     _check(rf, x, wq, np.ones(8, np.float32), form=form)
+
+
+_RNG_SHAPES = np.random.default_rng(8)
+RANDOM = [(int(_RNG_SHAPES.integers(1, 700)), int(_RNG_SHAPES.integers(1, 700)), 128 * int(_RNG_SHAPES.integers(1, 24)))
+          for _ in range(6)]
+
+
+@pytest.mark.parametrize("M,N,K", RANDOM)
+@pytest.mark.parametrize("form", FORMS)
+def test_random_shapes(rf, M, N, K, form):
+    """Seeded random shapes (codes and scales bit-exact, both forms bit-identical)."""
+    x, wq, ws = quant_inputs(M, N, K, seed=1700 + M + N + K)
+    _check(rf, x, wq, ws, form=form)
